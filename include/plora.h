@@ -1,0 +1,166 @@
+/*
+ * plora.h -- C ABI of the packed multi-LoRA linear operator for AMD MI355X
+ * (gfx950).
+ *
+ * The operator.  Many LoRA adapters, each with its own rank r_i, scale
+ * s_i = alpha_i / r_i and token segment S_i = [o_i, o_{i+1}), train together
+ * on one frozen linear layer W.  The LoRA branch is a down-projection A_i
+ * (d_in -> r_i) followed by an up-projection B_i (r_i -> d_out), scaled by
+ * alpha_i / r_i and added to the frozen layer's output
+ * [LLM+LoRA微调加速技术原理解析 (m.youleyou.com), 深入理解LoRA：基本原理与PEFT实现];
+ * W is frozen and only A and B receive gradients
+ * [LoRA加速集成方案 (cloud.baidu.com), 四、工作原理 > 3. 反向传播阶段];
+ * the adapters are packed on one shared base and their work is batched
+ * instead of run adapter by adapter, covering the forward and the backward
+ * gradient cases [PLoRA technical summary (gist.science, arXiv 2508.02932),
+ * 方法论 > 2. LoRA 执行引擎 > 打包 LoRA 算子 / 算子设计].
+ *
+ * For a token t in S_i (math orientation: W_m = W^T is d_in x d_out,
+ * A_i is d_in x r_i, B_i is r_i x d_out):
+ *
+ *   plora_forward        Y[t]  = X[t] W_m + s_i (X[t] A_i) B_i,  H_i[t] = X[t] A_i
+ *   plora_backward_dx    dX[t] = dY[t] W_m^T + s_i (dY[t] B_i^T) A_i^T,
+ *                        G_i[t] = dY[t] B_i^T
+ *   plora_backward_dAdB  dA_i = s_i X[S_i]^T G_i,  dB_i = s_i H_i^T dY[S_i]
+ *
+ * Storage (row-major, contiguous, device memory, 16-byte aligned):
+ *   X, dX  [T, d_in]        element type = desc.dtype
+ *   Y, dY  [T, d_out]       element type = desc.dtype
+ *   W      [d_out, d_in]    element type = desc.dtype (the nn.Linear weight;
+ *                           W_m = W^T)
+ *   A      [R, d_in]        rows R_off[i] .. R_off[i]+r_i-1 hold A_i^T
+ *                           (column j of A_i is row R_off[i]+j), R = sum r_i,
+ *                           R_off[i] = sum_{j<i} r_j
+ *   B      [R, d_out]       rows R_off[i] .. hold B_i
+ *   dA, dB fp32, laid out like A and B
+ *   H, G   fp32, plora_h_elems() elements; block i starts at
+ *          H_off[i] = sum_{j<i} n_j r_j and is [n_i, r_i] row-major
+ *
+ * Precision.  bf16: products of bf16 inputs are accumulated in fp32; H and G
+ * are fp32; each element of Y and dX is rounded once (round to nearest even)
+ * to bf16 from its fp32 accumulator; dA and dB are fp32.  f32: fp32 inputs,
+ * fp32 arithmetic throughout (no reduced-precision matrix modes).
+ *
+ * Ownership and side effects.  The caller owns every buffer.  The library
+ * allocates no device memory, keeps no per-call state, never synchronises and
+ * enqueues work only on `stream` (a hipStream_t; NULL means the null stream).
+ * Host arrays in the descriptor are read during the call only.  Inputs are
+ * never written.  Outputs (Y, H, dX, G, dA, dB) are overwritten, not
+ * accumulated.  One training step calls plora_forward (writes H), then
+ * plora_backward_dx (writes G), then plora_backward_dAdB (reads H and G).
+ *
+ * Errors.  Every entry point returns PLORA_OK (0) or a negative plora_status.
+ * All arguments are validated before anything is enqueued, so a call that
+ * fails validation has no side effects.  After PLORA_ERR_HIP the stream may
+ * hold part of the call's work.  plora_last_error() gives a message for the
+ * last failure on the calling thread.  No C++ exception crosses this ABI.
+ * Calls are reentrant; calls that share output buffers on overlapping
+ * streams race, as any two kernels writing one buffer would.
+ */
+#ifndef PLORA_H
+#define PLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PLORA_ABI_VERSION 1
+#define PLORA_MAX_ADAPTERS 64
+#define PLORA_MAX_RANK 128
+
+typedef enum {
+    PLORA_OK = 0,
+    PLORA_ERR_NULL = -1,      /* a required pointer is NULL */
+    PLORA_ERR_SEGMENTS = -2,  /* offsets not 0 = o_0 <= ... <= o_N = n_tokens */
+    PLORA_ERR_RANK = -3,      /* a rank outside 1..PLORA_MAX_RANK */
+    PLORA_ERR_ALPHA = -4,     /* a non-finite alpha */
+    PLORA_ERR_SHAPE = -5,     /* d_in/d_out not positive multiples of 8, n_tokens < 0 */
+    PLORA_ERR_ADAPTERS = -6,  /* n_adapters outside 0..PLORA_MAX_ADAPTERS */
+    PLORA_ERR_DTYPE = -7,     /* dtype not a plora_dtype */
+    PLORA_ERR_WORKSPACE = -8, /* workspace smaller than plora_workspace_bytes() */
+    PLORA_ERR_ALIGN = -9,     /* a device pointer not 16-byte aligned */
+    PLORA_ERR_HIP = -10       /* a HIP runtime call or kernel launch failed */
+} plora_status;
+
+typedef enum { PLORA_F32 = 0, PLORA_BF16 = 1 } plora_dtype;
+
+/* Problem descriptor.  All pointers are HOST pointers.
+ *   n_adapters   N, 0..64.  N = 0 runs the frozen path only (Y = X W_m,
+ *                dX = dY W_m^T); H, G, A, B may then be NULL.
+ *   dtype        plora_dtype of X, W, A, B, Y, dY, dX.
+ *   n_tokens     T >= 0.  T = 0 makes every call a no-op.
+ *   d_in, d_out  positive multiples of 8.
+ *   seg_offsets  N+1 int64: o_0 = 0, non-decreasing, o_N = T; empty
+ *                segments are allowed (that adapter gets dA_i = dB_i = 0).
+ *   ranks        N int32 in 1..128.
+ *   alphas       N finite floats; s_i = alphas[i] / ranks[i] in fp32. */
+typedef struct {
+    int32_t n_adapters;
+    int32_t dtype;
+    int64_t n_tokens;
+    int64_t d_in;
+    int64_t d_out;
+    const int64_t* seg_offsets;
+    const int32_t* ranks;
+    const float* alphas;
+} plora_desc;
+
+/* Forward: Y = X W_m + concat_i[ s_i (X[S_i] A_i) B_i ], and H (fp32) for the
+ * weight-gradient pass.  Y and H are overwritten. */
+int plora_forward(const plora_desc* desc, const void* X, const void* W, const void* A,
+                  const void* B, void* Y, float* H, void* stream);
+
+/* Backward through the activations: dX = dY W_m^T + concat_i[ s_i G_i A_i^T ]
+ * with G_i = dY[S_i] B_i^T, and G (fp32) for the weight-gradient pass. */
+int plora_backward_dx(const plora_desc* desc, const void* dY, const void* W, const void* A,
+                      const void* B, void* dX, float* G, void* stream);
+
+/* Backward to the adapters: dA_i = s_i X[S_i]^T G_i and dB_i = s_i H_i^T dY[S_i]
+ * (fp32, layouts of A and B), reducing over each adapter's tokens.  H and G are
+ * the buffers written by plora_forward and plora_backward_dx.  `workspace`
+ * must hold plora_workspace_bytes(desc) bytes (it may be NULL when that is
+ * 0); its contents on entry do not matter.  The reduction order is fixed, so
+ * results are bitwise reproducible run to run. */
+int plora_backward_dAdB(const plora_desc* desc, const void* X, const void* dY, const float* H,
+                        const float* G, float* dA, float* dB, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Number of fp32 elements of H (and of G): sum_i n_i r_i.  Returns 0 for an
+ * invalid descriptor. */
+size_t plora_h_elems(const plora_desc* desc);
+
+/* Bytes of workspace plora_backward_dAdB needs for this descriptor (0 when no
+ * adapter's tokens are split across work items).  Returns 0 for an invalid
+ * descriptor. */
+size_t plora_workspace_bytes(const plora_desc* desc);
+
+/* Validates a descriptor without touching the GPU; returns a plora_status. */
+int plora_validate(const plora_desc* desc);
+
+/* Human-readable name of a plora_status. */
+const char* plora_status_string(int status);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* plora_last_error(void);
+
+/* PLORA_ABI_VERSION of the loaded library. */
+int plora_version(void);
+
+/* Kernel timing.  With profiling on, the library records a HIP event pair
+ * on the call's stream around every kernel it launches (kernel classes:
+ * "shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce").  After the caller has
+ * synchronised the stream, plora_profile_read returns the number of launches
+ * and their summed duration in milliseconds for one class.  Profiling is a
+ * process-wide switch meant for benchmarks; it is not thread-safe. */
+int plora_profile_enable(int on);
+int plora_profile_read(const char* kernel_class, int* launches, double* total_ms);
+void plora_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLORA_H */

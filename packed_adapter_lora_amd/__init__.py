@@ -1,0 +1,225 @@
+"""Python binding of libplora.so, the packed multi-LoRA operator for MI355X.
+
+Argument marshalling only: every step of the operator runs in the HIP
+kernels behind the C ABI declared in ``include/plora.h``.  The functions keep
+the C names.  Device buffers are passed as torch tensors (their
+``data_ptr()``) or raw integer addresses; the stream defaults to torch's
+current stream.  There is no fallback: if ``libplora.so`` is missing, loading
+this package raises.
+
+    desc = Desc(offsets, ranks, alphas, d_in, d_out, "bf16")
+    plora_forward(desc, X, W, A, B, Y, H)
+    plora_backward_dx(desc, dY, W, A, B, dX, G)
+    plora_backward_dAdB(desc, X, dY, H, G, dA, dB, ws)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
+    "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version",
+    "plora_profile_enable", "plora_profile_read", "plora_profile_reset", "LIB_PATH", "PLORA_F32", "PLORA_BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libplora.so")
+PLORA_F32, PLORA_BF16 = 0, 1
+_DTYPES = {"f32": PLORA_F32, "float32": PLORA_F32, "bf16": PLORA_BF16, "bfloat16": PLORA_BF16}
+
+
+class plora_desc(ctypes.Structure):
+    _fields_ = [
+        ("n_adapters", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("n_tokens", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("d_out", ctypes.c_int64),
+        ("seg_offsets", ctypes.POINTER(ctypes.c_int64)),
+        ("ranks", ctypes.POINTER(ctypes.c_int32)),
+        ("alphas", ctypes.POINTER(ctypes.c_float)),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libplora.so is not built (run: python -m packed_adapter_lora_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, dp = ctypes.c_void_p, ctypes.POINTER(plora_desc)
+    fp = ctypes.c_void_p
+    sig = {
+        "plora_forward": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, fp, vp]),
+        "plora_backward_dx": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, fp, vp]),
+        "plora_backward_dAdB": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]),
+        "plora_h_elems": (ctypes.c_size_t, [dp]),
+        "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
+        "plora_validate": (ctypes.c_int, [dp]),
+        "plora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "plora_last_error": (ctypes.c_char_p, []),
+        "plora_version": (ctypes.c_int, []),
+        "plora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+        "plora_profile_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
+                                              ctypes.POINTER(ctypes.c_double)]),
+        "plora_profile_reset": (None, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+
+
+class PloraError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (plora_status_string(status), status, msg))
+        self.status = status
+
+
+class Desc:
+    """Owns the host arrays of a ``plora_desc`` (offsets int64, ranks int32, alphas fp32)."""
+
+    def __init__(self, offsets, ranks, alphas, d_in, d_out, dtype="bf16", n_tokens=None):
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.ranks = np.ascontiguousarray(ranks, dtype=np.int32)
+        self.alphas = np.ascontiguousarray(alphas, dtype=np.float32)
+        n = int(self.ranks.shape[0])
+        if self.offsets.shape[0] < 1:
+            self.offsets = np.zeros(1, np.int64)
+        T = int(self.offsets[-1]) if n_tokens is None else int(n_tokens)
+        self.dtype = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+        self.c = plora_desc(n, self.dtype, T, int(d_in), int(d_out),
+                            self.offsets.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                            self.ranks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                            self.alphas.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+
+    @classmethod
+    def from_workload(cls, wl):
+        return cls(wl.offsets, wl.ranks, wl.alphas, wl.d_in, wl.d_out, wl.dtype, wl.T)
+
+    @property
+    def n_tokens(self):
+        return int(self.c.n_tokens)
+
+    @property
+    def R(self):
+        return int(self.ranks.sum())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PloraError(rc, (_lib.plora_last_error() or b"").decode())
+
+
+def _check_tensor(name, t, shape, dtype):
+    """Shape/dtype/layout check of a torch tensor against the descriptor."""
+    if t is None or isinstance(t, int):
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and str(t.dtype).split(".")[-1] != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _elt(desc):
+    return "bfloat16" if desc.dtype == PLORA_BF16 else "float32"
+
+
+def plora_forward(desc: Desc, X, W, A, B, Y, H, stream=None):
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    for n, t, s, d in (("X", X, (T, di), e), ("W", W, (do, di), e), ("A", A, (R, di), e), ("B", B, (R, do), e),
+                       ("Y", Y, (T, do), e), ("H", H, (plora_h_elems(desc),), "float32")):
+        _check_tensor(n, t, s, d)
+    _check(_lib.plora_forward(desc.ref(), _addr(X), _addr(W), _addr(A), _addr(B), _addr(Y), _addr(H),
+                              _stream(stream)))
+
+
+def plora_backward_dx(desc: Desc, dY, W, A, B, dX, G, stream=None):
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    for n, t, s, d in (("dY", dY, (T, do), e), ("W", W, (do, di), e), ("A", A, (R, di), e), ("B", B, (R, do), e),
+                       ("dX", dX, (T, di), e), ("G", G, (plora_h_elems(desc),), "float32")):
+        _check_tensor(n, t, s, d)
+    _check(_lib.plora_backward_dx(desc.ref(), _addr(dY), _addr(W), _addr(A), _addr(B), _addr(dX), _addr(G),
+                                  _stream(stream)))
+
+
+def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=None):
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    he = plora_h_elems(desc)
+    for n, t, s, d in (("X", X, (T, di), e), ("dY", dY, (T, do), e), ("H", H, (he,), "float32"),
+                       ("G", G, (he,), "float32"), ("dA", dA, (R, di), "float32"), ("dB", dB, (R, do), "float32")):
+        _check_tensor(n, t, s, d)
+    nbytes = 0
+    if workspace is not None and not isinstance(workspace, int):
+        nbytes = workspace.numel() * workspace.element_size()
+    elif isinstance(workspace, int):
+        nbytes = plora_workspace_bytes(desc)
+    _check(_lib.plora_backward_dAdB(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA), _addr(dB),
+                                    _addr(workspace), nbytes, _stream(stream)))
+
+
+def plora_h_elems(desc: Desc) -> int:
+    return int(_lib.plora_h_elems(desc.ref()))
+
+
+def plora_workspace_bytes(desc: Desc) -> int:
+    return int(_lib.plora_workspace_bytes(desc.ref()))
+
+
+def plora_validate(desc: Desc) -> int:
+    return int(_lib.plora_validate(desc.ref()))
+
+
+def plora_status_string(status: int) -> str:
+    return _lib.plora_status_string(int(status)).decode()
+
+
+def plora_last_error() -> str:
+    return (_lib.plora_last_error() or b"").decode()
+
+
+def plora_version() -> int:
+    return int(_lib.plora_version())
+
+
+def plora_profile_enable(on: bool = True):
+    _check(_lib.plora_profile_enable(1 if on else 0))
+
+
+def plora_profile_read(kernel_class: str):
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(_lib.plora_profile_read(kernel_class.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+def plora_profile_reset():
+    _lib.plora_profile_reset()

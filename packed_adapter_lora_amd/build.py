@@ -1,0 +1,65 @@
+"""Build libplora.so in-tree for gfx950 (hipcc) -- no JIT, no torch extension.
+
+    python -m packed_adapter_lora_amd.build
+
+Every HIP source is compiled with packed-fp32 instructions disabled (the
+compiler otherwise forms v_pk_* fp32 ops from ordinary float code).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libplora.so")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["api.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip"]
+CXX_SOURCES = ["plan.cpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", INCLUDE, "-I", CSRC]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass of hipcc does not know the packed-fp32 feature; that note is harmless
+    out = "\n".join(ln for ln in r.stdout.splitlines() if "packed-fp32-ops" not in ln)
+    if r.returncode != 0:
+        raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), out))
+    return out
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs_list = []
+    for s in HIP_SOURCES:
+        obj = os.path.join(BUILD, s + ".o")
+        jobs_list.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])
+    for s in CXX_SOURCES:
+        obj = os.path.join(BUILD, s + ".o")
+        jobs_list.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(jobs_list)))) as ex:
+        outs = list(ex.map(_run, jobs_list))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    objs = [os.path.join(BUILD, s + ".o") for s in HIP_SOURCES + CXX_SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,279 @@
+// api.hip -- the C ABI of the packed multi-LoRA operator (see include/plora.h).
+//
+// Each entry point validates everything on the host first (no side effects on
+// failure), builds the per-adapter table and work maps, and enqueues its
+// kernels on the caller's stream.  No device memory is allocated and nothing
+// is synchronised.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+#include "plan.h"
+#include "plora.h"
+
+namespace plora {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& why) {
+    g_last_error = std::string(plora_status_string(status)) + ": " + why;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PLORA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// ---- kernel timing (process-wide switch for benchmarks) ----------------------
+struct ProfRec {
+    std::string cls;
+    hipEvent_t a, b;
+};
+struct Prof {
+    bool on = false;
+    std::vector<ProfRec> recs;
+    std::vector<hipEvent_t> pool;
+    std::mutex mu;
+} g_prof;
+
+hipEvent_t take_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class Fn>
+hipError_t timed(const char* cls, hipStream_t st, Fn&& fn) {
+    if (!g_prof.on) return fn();
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    hipEvent_t a = take_event(), b = take_event();
+    if (a) (void)hipEventRecord(a, st);
+    const hipError_t e = fn();
+    if (b) (void)hipEventRecord(b, st);
+    if (a && b) g_prof.recs.push_back({cls, a, b});
+    return e;
+}
+
+int check_common(const plora_desc* d) {
+    const char* why = "";
+    const int rc = validate_desc(d, &why);
+    if (rc != PLORA_OK) return fail(rc, why);
+    return PLORA_OK;
+}
+
+}  // namespace
+}  // namespace plora
+
+using namespace plora;
+
+extern "C" {
+
+const char* plora_status_string(int s) {
+    switch (s) {
+        case PLORA_OK: return "PLORA_OK";
+        case PLORA_ERR_NULL: return "PLORA_ERR_NULL";
+        case PLORA_ERR_SEGMENTS: return "PLORA_ERR_SEGMENTS";
+        case PLORA_ERR_RANK: return "PLORA_ERR_RANK";
+        case PLORA_ERR_ALPHA: return "PLORA_ERR_ALPHA";
+        case PLORA_ERR_SHAPE: return "PLORA_ERR_SHAPE";
+        case PLORA_ERR_ADAPTERS: return "PLORA_ERR_ADAPTERS";
+        case PLORA_ERR_DTYPE: return "PLORA_ERR_DTYPE";
+        case PLORA_ERR_WORKSPACE: return "PLORA_ERR_WORKSPACE";
+        case PLORA_ERR_ALIGN: return "PLORA_ERR_ALIGN";
+        case PLORA_ERR_HIP: return "PLORA_ERR_HIP";
+        default: return "PLORA_ERR_UNKNOWN";
+    }
+}
+
+const char* plora_last_error(void) { return g_last_error.c_str(); }
+
+int plora_version(void) { return PLORA_ABI_VERSION; }
+
+int plora_validate(const plora_desc* d) {
+    const char* why = "";
+    return validate_desc(d, &why);
+}
+
+size_t plora_h_elems(const plora_desc* d) {
+    if (plora_validate(d) != PLORA_OK) return 0;
+    SegTable s;
+    build_segtable(d, &s);
+    return (size_t)s.hoff[s.n];
+}
+
+size_t plora_workspace_bytes(const plora_desc* d) {
+    if (plora_validate(d) != PLORA_OK) return 0;
+    if (d->dtype == PLORA_F32) return 0;
+    SegTable s;
+    build_segtable(d, &s);
+    return workspace_bytes(s, d->d_in, d->d_out);
+}
+
+int plora_forward(const plora_desc* d, const void* X, const void* W, const void* A, const void* B, void* Y,
+                  float* H, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_tokens == 0) return PLORA_OK;
+        const bool lora = d->n_adapters > 0;
+        if (!X || !W || !Y) return fail(PLORA_ERR_NULL, "X, W and Y are required");
+        if (lora && (!A || !B || !H)) return fail(PLORA_ERR_NULL, "A, B and H are required when n_adapters > 0");
+        if (misaligned(X) || misaligned(W) || misaligned(Y) || (lora && (misaligned(A) || misaligned(B) || misaligned(H))))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const bool bf = d->dtype == PLORA_BF16;
+        hipError_t e = hipSuccess;
+        if (lora) {
+            const ShrinkArgs sa{X, A, H, d->d_in};
+            if (bf) {
+                WorkMap m;
+                const int32_t units = build_shrink_map(s, &m);
+                e = timed("shrink", st, [&] { return launch_shrink_bf16(sa, s, m, units, st); });
+            } else {
+                e = timed("shrink", st, [&] { return launch_shrink_f32(sa, s, st); });
+            }
+            if (e != hipSuccess) return hip_fail(e, "shrink launch");
+        }
+        const GemmArgs ga{W, X, B, H, Y, d->n_tokens, d->d_in, d->d_out, lora ? 1 : 0};
+        e = timed("gemm_fwd", st, [&] { return bf ? launch_gemm_bf16(true, ga, s, st) : launch_gemm_f32(true, ga, s, st); });
+        if (e != hipSuccess) return hip_fail(e, "gemm launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_backward_dx(const plora_desc* d, const void* dY, const void* W, const void* A, const void* B, void* dX,
+                      float* G, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_tokens == 0) return PLORA_OK;
+        const bool lora = d->n_adapters > 0;
+        if (!dY || !W || !dX) return fail(PLORA_ERR_NULL, "dY, W and dX are required");
+        if (lora && (!A || !B || !G)) return fail(PLORA_ERR_NULL, "A, B and G are required when n_adapters > 0");
+        if (misaligned(dY) || misaligned(W) || misaligned(dX) ||
+            (lora && (misaligned(A) || misaligned(B) || misaligned(G))))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const bool bf = d->dtype == PLORA_BF16;
+        hipError_t e = hipSuccess;
+        if (lora) {
+            const ShrinkArgs sa{dY, B, G, d->d_out};
+            if (bf) {
+                WorkMap m;
+                const int32_t units = build_shrink_map(s, &m);
+                e = timed("shrink", st, [&] { return launch_shrink_bf16(sa, s, m, units, st); });
+            } else {
+                e = timed("shrink", st, [&] { return launch_shrink_f32(sa, s, st); });
+            }
+            if (e != hipSuccess) return hip_fail(e, "shrink launch");
+        }
+        // dX[t][k] = sum_n dY[t][n] W[n][k] + ...: P(p = k, kk = n) = W[n][k] is p-contiguous.
+        const GemmArgs ga{W, dY, A, G, dX, d->n_tokens, d->d_out, d->d_in, lora ? 1 : 0};
+        e = timed("gemm_bwd", st, [&] { return bf ? launch_gemm_bf16(false, ga, s, st) : launch_gemm_f32(false, ga, s, st); });
+        if (e != hipSuccess) return hip_fail(e, "gemm launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, const float* H, const float* G, float* dA,
+                        float* dB, void* ws, size_t ws_bytes, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_adapters == 0) return PLORA_OK;
+        if (!dA || !dB) return fail(PLORA_ERR_NULL, "dA and dB are required");
+        if (d->n_tokens > 0 && (!X || !dY || !H || !G)) return fail(PLORA_ERR_NULL, "X, dY, H and G are required");
+        if (misaligned(X) || misaligned(dY) || misaligned(H) || misaligned(G) || misaligned(dA) || misaligned(dB))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        hipError_t e = hipSuccess;
+        if (d->dtype == PLORA_F32) {
+            const WgradArgs wb{dY, H, dB, nullptr, d->d_out};
+            const WgradArgs wa{X, G, dA, nullptr, d->d_in};
+            e = timed("wgrad", st, [&] { return launch_wgrad_f32(wb, s, st); });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            e = timed("wgrad", st, [&] { return launch_wgrad_f32(wa, s, st); });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            return PLORA_OK;
+        }
+        const size_t need = workspace_bytes(s, d->d_in, d->d_out);
+        if (ws_bytes < need || (need > 0 && !ws))
+            return fail(PLORA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+        if (need > 0 && misaligned(ws)) return fail(PLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
+        WgradPlan pa, pb;
+        build_wgrad_plan(s, d->d_in, &pa);
+        build_wgrad_plan(s, d->d_out, &pb);
+        float* part_a = static_cast<float*>(ws);
+        float* part_b = part_a ? part_a + (((size_t)pa.part_elems * 4 + 255) & ~(size_t)255) / 4 : nullptr;
+        const WgradArgs wb{dY, H, dB, part_b, d->d_out};
+        const WgradArgs wa{X, G, dA, part_a, d->d_in};
+        e = timed("wgrad", st, [&] { return launch_wgrad_bf16(wb, s, pb, st); });
+        if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+        e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
+        if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        e = timed("wgrad", st, [&] { return launch_wgrad_bf16(wa, s, pa, st); });
+        if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+        e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
+        if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_profile_enable(int on) {
+    g_prof.on = on != 0;
+    return PLORA_OK;
+}
+
+int plora_profile_read(const char* cls, int* launches, double* total_ms) {
+    if (!cls || !launches || !total_ms) return fail(PLORA_ERR_NULL, "profile_read arguments");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    int n = 0;
+    double ms = 0.0;
+    for (auto& r : g_prof.recs) {
+        if (r.cls != cls) continue;
+        float t = 0.0f;
+        const hipError_t e = hipEventElapsedTime(&t, r.a, r.b);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        ++n;
+        ms += t;
+    }
+    *launches = n;
+    *total_ms = ms;
+    return PLORA_OK;
+}
+
+void plora_profile_reset(void) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (auto& r : g_prof.recs) {
+        g_prof.pool.push_back(r.a);
+        g_prof.pool.push_back(r.b);
+    }
+    g_prof.recs.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,310 @@
+// lora_bf16.hip -- segment-indexed LoRA kernels that are not fused into the
+// base GEMM (gfx950, bf16 in, fp32 out).
+//
+//   shrink   H_i = X[S_i] A_i          G_i = dY[S_i] B_i^T           (n_i x r_i)
+//   wgrad    dA_i = s_i X[S_i]^T G_i   dB_i = s_i H_i^T dY[S_i]      (reduce over tokens)
+//
+// These are the down-projection and the two weight-gradient cases of the
+// packed operators [PLoRA technical summary (gist.science, arXiv
+// 2508.02932), 方法论 > 2. LoRA 执行引擎 > 算子设计: tile the concatenated
+// LoRA tensors along tokens or hidden features, not rank; balance load across
+// heterogeneous adapters], for the LoRA branch X A B scaled by alpha/r with
+// gradients only for A and B [LLM+LoRA微调加速技术原理解析, 深入理解LoRA;
+// LoRA加速集成方案, 四、工作原理 > 3. 反向传播阶段].
+//
+// Both stream one large activation (X or dY) once from HBM and are bound by
+// HBM bandwidth (about r flop per byte).  Work is cut into equal token tiles
+// per adapter (32 rows for shrink, a fixed token chunk x 256 features for the
+// weight gradients), so adapters with 16x more tokens get 16x more work items
+// rather than a 16x longer one.
+#include "device_common.h"
+#include "launch.h"
+
+namespace plora {
+namespace {
+
+// ---------------------------------------------------------------------------
+// shrink: one wavefront per 32-token tile of one adapter; MFMA A = token rows,
+// MFMA B = rank rows of the packed panel (r padded to 32 with zeros).  Lane l
+// reads k = kb + 32*(l/32) + 8*s (s = 0..3) of its row, so the two half-waves
+// together read each row's 128-byte block.  No LDS, no barriers.
+// ---------------------------------------------------------------------------
+template <int MAXJT>
+__global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, WorkMap m, int32_t units) {
+    const int gw = (int)blockIdx.x * 4 + wave_id();
+    if (gw >= units) return;
+    const bf16* __restrict__ Q = static_cast<const bf16*>(a.Q);
+    const bf16* __restrict__ P = static_cast<const bf16*>(a.P);
+    const int64_t K = a.K;
+    const int i = adapter_of_unit(m, seg.n, gw);
+    const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
+    const int64_t t0 = s0 + (int64_t)(gw - m.pre[i]) * kShrinkRows;
+    const int nrows = (int)(s1 - t0 < kShrinkRows ? s1 - t0 : kShrinkRows);
+    const int r = seg.rank[i];
+    const int ntj = (r + 31) >> 5;
+    const int l = lane_id(), l32 = l & 31, lh = l >> 5;
+
+    const bf16* qrow = Q + (t0 + (l32 < nrows ? l32 : nrows - 1)) * K + 32 * lh;
+    const bf16* prow[MAXJT];
+    bool pv[MAXJT];
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) {
+        const int j = jt * 32 + l32;
+        pv[jt] = j < r;
+        prow[jt] = P + ((int64_t)seg.roff[i] + (pv[jt] ? j : 0)) * K + 32 * lh;
+    }
+
+    f32x16 acc[MAXJT];
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = f32x16{};
+
+    u32x4 xq[2][4], ap[2][MAXJT][4];
+    auto load = [&](int buf, int64_t kb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bool ok = kb + 32 * lh + 8 * s < K;
+            xq[buf][s] = load16_or_zero(qrow + kb + 8 * s, ok);
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt)
+                ap[buf][jt][s] = load16_or_zero(prow[jt] + kb + 8 * s, ok && pv[jt]);
+        }
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt)
+                if (jt < ntj) acc[jt] = mfma32x32x16(as_bf16x8(xq[buf][s]), as_bf16x8(ap[buf][jt][s]), acc[jt]);
+    };
+    // two register buffers, unrolled so each buffer index is a constant
+    load(0, 0);
+    for (int64_t kb = 0; kb < K; kb += 128) {
+        if (kb + 64 < K) load(1, kb + 64);
+        mma(0);
+        if (kb + 64 >= K) break;
+        if (kb + 128 < K) load(0, kb + 128);
+        mma(1);
+    }
+
+    float* __restrict__ out = a.out + seg.hoff[i] + (t0 - s0) * r;
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) {
+        const int j = jt * 32 + l32;
+        if (jt >= ntj || j >= r) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
+            if (row < nrows) out[(int64_t)row * r + j] = acc[jt][v];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// wgrad: one workgroup per (adapter token chunk, 256 features).  MFMA
+// A = rank rows (from fp32 H/G, s folded in later, split into bf16 hi + lo),
+// MFMA B = feature columns of X/dY, K = tokens, 32 tokens per stage.
+// ---------------------------------------------------------------------------
+constexpr int kWgTok = 32;                   // tokens per stage
+constexpr int kWgCols = 256;                 // features per workgroup
+constexpr int kQRow = kWgCols * 2 + 16;      // LDS row of the activation tile (padded)
+constexpr int kQTile = kWgTok * kQRow;       // 16896 B
+constexpr int kFRow = kWgTok * 2;            // LDS row of the H/G tile: 32 tokens bf16
+constexpr int kFTile = 128 * kFRow;          // up to 128 rank rows: 8 KiB
+constexpr int kWgStage = kQTile + 2 * kFTile;
+
+__device__ __forceinline__ int fofs(int j, int c) { return j * kFRow + ((c ^ ((j >> 1) & 3)) << 4); }
+
+template <int MAXJT>
+__global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, WgradPlan plan) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kWgStage];
+    const bf16* __restrict__ Q = static_cast<const bf16*>(a.Q);
+    const int64_t D = a.D;
+    const int w = (int)blockIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.y * kWgCols;
+    const int i = adapter_of_unit(plan.chunks, seg.n, w);
+    const int u = w - plan.chunks.pre[i];
+    const int nchunks = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
+    const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
+    const int64_t ta = s0 + (int64_t)u * plan.chunk_tokens;
+    const int64_t tb = ta + plan.chunk_tokens < s1 ? ta + plan.chunk_tokens : s1;
+    const int r = seg.rank[i];
+    const int ntj = (r + 31) >> 5;
+    const int rp = ntj * 32;
+    const float* __restrict__ Fi = a.F + seg.hoff[i];
+
+    const int tid = (int)threadIdx.x, l = lane_id(), wv = wave_id();
+    const int l32 = l & 31, lh = l >> 5;
+
+    f32x16 acc[MAXJT][2];
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) acc[jt][0] = acc[jt][1] = f32x16{};
+
+    // staging registers: 4 activation chunks + up to 2 H/G tasks per thread
+    u32x4 qv[4];
+    u16x8 fh[2], fl[2];
+    const int q_row = tid >> 5, q_pc = tid & 31;
+    auto gload = [&](int64_t tt) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int64_t t = tt + it * 8 + q_row;
+            const int64_t c = c0 + q_pc * 8;
+            qv[it] = load16_or_zero(Q + t * D + c, t < tb && c < D);
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int task = tid + it * 256;      // (rank row j, 8-token chunk tc)
+            const int j = task >> 2, tc = task & 3;
+            u16x8 h, o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t t = tt + tc * 8 + e;
+                const float v = (j < r && t < tb) ? Fi[(t - s0) * r + j] : 0.0f;
+                bf16 hb, lb;
+                split_bf16(v, hb, lb);
+                h[e] = __builtin_bit_cast(uint16_t, hb);
+                o[e] = __builtin_bit_cast(uint16_t, lb);
+            }
+            fh[it] = h;
+            fl[it] = o;
+        }
+    };
+    auto lstore = [&](int buf) {
+        uint8_t* sq = smem + buf * kWgStage;
+        uint8_t* sh = sq + kQTile;
+        uint8_t* sl = sh + kFTile;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) *reinterpret_cast<u32x4*>(sq + (it * 8 + q_row) * kQRow + q_pc * 16) = qv[it];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int task = tid + it * 256;
+            const int j = task >> 2, tc = task & 3;
+            if (j < rp) {
+                *reinterpret_cast<u16x8*>(sh + fofs(j, tc)) = fh[it];
+                *reinterpret_cast<u16x8*>(sl + fofs(j, tc)) = fl[it];
+            }
+        }
+    };
+    auto compute = [&](int buf) {
+        const uint8_t* sq = smem + buf * kWgStage;
+        const uint8_t* sh = sq + kQTile;
+        const uint8_t* sl = sh + kFTile;
+#pragma unroll
+        for (int kk = 0; kk < kWgTok / 16; ++kk) {
+            bf16x8 qf[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int c = wv * 64 + ct * 32 + l32;
+                u16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = *reinterpret_cast<const uint16_t*>(sq + (16 * kk + 8 * lh + e) * kQRow + c * 2);
+                qf[ct] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt) {
+                if (jt >= ntj) continue;
+                const int j = jt * 32 + l32;
+                const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(sh + fofs(j, 2 * kk + lh)));
+                const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + fofs(j, 2 * kk + lh)));
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[jt][ct] = mfma32x32x16(ah, qf[ct], acc[jt][ct]);
+                    acc[jt][ct] = mfma32x32x16(al, qf[ct], acc[jt][ct]);
+                }
+            }
+        }
+    };
+
+    const int nst = (int)((tb - ta + kWgTok - 1) / kWgTok);
+    gload(ta);
+    lstore(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int cur = st & 1;
+        if (st + 1 < nst) gload(ta + (int64_t)(st + 1) * kWgTok);
+        compute(cur);
+        if (st + 1 < nst) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // D[j][c]: lane holds feature column c, rank rows 8*(v/4) + 4*(l/32) + v%4.
+    const bool direct = nchunks == 1;
+    const float sc = seg.scale[i];
+    float* __restrict__ dst = direct ? a.out + (int64_t)seg.roff[i] * D
+                                     : a.part + plan.part_off[i] + (int64_t)u * r * D;
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) {
+        if (jt >= ntj) continue;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int64_t c = c0 + wv * 64 + ct * 32 + l32;
+            if (c >= D) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if (j < r) dst[(int64_t)j * D + c] = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+            }
+        }
+    }
+}
+
+// out rows of adapters whose tokens span 0 or >= 2 chunks:
+// out = s_i * sum_u partial[u] in chunk order (0 for an empty adapter).
+__global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, WgradPlan plan) {
+    const int i = (int)blockIdx.y;
+    const int nch = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
+    if (nch == 1) return;
+    const int64_t n = (int64_t)seg.rank[i] * a.D;  // multiple of 8
+    const float sc = seg.scale[i];
+    float* __restrict__ out = a.out + (int64_t)seg.roff[i] * a.D;
+    const float* __restrict__ part = a.part + plan.part_off[i];
+    for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 1024) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < nch; ++u) s += *reinterpret_cast<const f32x4*>(part + (int64_t)u * n + e);
+        *reinterpret_cast<f32x4*>(out + e) = s * sc;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
+                              hipStream_t st) {
+    if (units <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+    const int jt = (s.rmax + 31) / 32;
+    switch (jt) {
+        case 1: hipLaunchKernelGGL(shrink_bf16<1>, grid, block, 0, st, a, s, m, units); break;
+        case 2: hipLaunchKernelGGL(shrink_bf16<2>, grid, block, 0, st, a, s, m, units); break;
+        case 3: hipLaunchKernelGGL(shrink_bf16<3>, grid, block, 0, st, a, s, m, units); break;
+        default: hipLaunchKernelGGL(shrink_bf16<4>, grid, block, 0, st, a, s, m, units); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st) {
+    const int32_t units = p.chunks.pre[s.n];
+    if (units <= 0) return hipSuccess;
+    const dim3 grid((unsigned)units, (unsigned)p.col_tiles), block(256);
+    const int jt = (s.rmax + 31) / 32;
+    switch (jt) {
+        case 1: hipLaunchKernelGGL(wgrad_bf16<1>, grid, block, 0, st, a, s, p); break;
+        case 2: hipLaunchKernelGGL(wgrad_bf16<2>, grid, block, 0, st, a, s, p); break;
+        case 3: hipLaunchKernelGGL(wgrad_bf16<3>, grid, block, 0, st, a, s, p); break;
+        default: hipLaunchKernelGGL(wgrad_bf16<4>, grid, block, 0, st, a, s, p); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st) {
+    bool any = false;
+    for (int i = 0; i < s.n; ++i) any |= (p.chunks.pre[i + 1] - p.chunks.pre[i]) != 1;
+    if (!any || s.n == 0) return hipSuccess;
+    const int64_t n = (int64_t)s.rmax * a.D;
+    int64_t bx = (n / 4 + 255) / 256;
+    if (bx > 1024) bx = 1024;
+    const dim3 grid((unsigned)bx, (unsigned)s.n), block(256);
+    hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, a, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace plora

@@ -1,0 +1,76 @@
+// plan.h -- host-side planning for the packed multi-LoRA operator.
+//
+// Plain C++ (no HIP headers): descriptor validation, the per-adapter tables
+// every kernel receives by value (segment offsets, rank prefix, H/G block
+// offsets, scales), and the work maps that cut each adapter's tokens into
+// fixed-size tiles so that a launch covers all adapters at once and no tile
+// straddles two adapters.  Tiling runs along tokens and hidden features,
+// never along the small rank dimension [PLoRA technical summary (gist.science,
+// arXiv 2508.02932), 方法论 > 2. LoRA 执行引擎 > 算子设计].
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "plora.h"
+
+namespace plora {
+
+constexpr int kMaxN = PLORA_MAX_ADAPTERS;
+constexpr int kMaxRank = PLORA_MAX_RANK;
+
+// Token rows per shrink work unit (one wavefront computes a 32-row tile).
+constexpr int kShrinkRows = 32;
+
+// Per-adapter table, passed to kernels by value (about 1.8 KiB of kernel
+// arguments; N <= 64 keeps it well under the 4 KiB argument limit, so no
+// device-side metadata buffer or host-to-device copy is needed).
+struct SegTable {
+    int32_t n;       // adapters
+    int32_t rmax;    // largest rank
+    int64_t T;       // tokens
+    int64_t off[kMaxN + 1];   // segment offsets o_i
+    int64_t hoff[kMaxN + 1];  // H/G block offsets: sum_{j<i} n_j r_j
+    int32_t roff[kMaxN + 1];  // rank prefix R_off[i]
+    int32_t rank[kMaxN];
+    float scale[kMaxN];       // alpha_i / r_i (fp32)
+};
+
+// Prefix sums of per-adapter work units (tiles or token chunks).
+struct WorkMap {
+    int32_t pre[kMaxN + 1];
+};
+
+// Weight-gradient plan for one reduction (dA over d_in or dB over d_out).
+struct WgradPlan {
+    int32_t chunk_tokens;      // tokens per work item (fixed per feature width)
+    int32_t col_tiles;         // ceil(D / 256)
+    WorkMap chunks;            // token chunks per adapter
+    int64_t part_off[kMaxN + 1];  // fp32 element offset of adapter i's partials
+    int64_t part_elems;        // total partial elements
+};
+
+// Returns a plora_status; checks only the descriptor (no pointers to data).
+int validate_desc(const plora_desc* d, const char** why);
+
+// Fills the segment table of a validated descriptor.
+void build_segtable(const plora_desc* d, SegTable* s);
+
+// Shrink tiles: ceil(n_i / kShrinkRows) per adapter.  Returns the total.
+int32_t build_shrink_map(const SegTable& s, WorkMap* m);
+
+// Token-chunk size of the weight-gradient reduction over a feature width D.
+// It depends only on D, so an adapter's reduction order is the same whether
+// it is packed with others or run alone.
+int32_t wgrad_chunk_tokens(int64_t D);
+
+// Plan one weight-gradient reduction over feature width D.  Adapters whose
+// tokens span more than one chunk get fp32 partials (chunks * r_i * D
+// elements); the rest are written directly.
+void build_wgrad_plan(const SegTable& s, int64_t D, WgradPlan* p);
+
+// Workspace bytes of plora_backward_dAdB: partials of dA and dB, each rounded
+// up to 256 bytes.
+size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out);
+
+}  // namespace plora

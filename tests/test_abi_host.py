@@ -1,0 +1,173 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads on a machine without a GPU; validation runs entirely on the
+host before anything is enqueued, so every error path is exercised here with
+descriptors and pointer values that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "plora.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    pkg = pytest.importorskip("packed_adapter_lora_amd")
+    return pkg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(plora_[a-z_A-Z0-9]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
+              "plora_workspace_bytes", "plora_status_string", "plora_last_error", "plora_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(P):
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(P):
+    assert P.plora_version() == 1
+    assert P.plora_status_string(0) == "PLORA_OK"
+    assert P.plora_status_string(-8) == "PLORA_ERR_WORKSPACE"
+    assert P.plora_status_string(12345) == "PLORA_ERR_UNKNOWN"
+
+
+def desc(P, counts=(3, 0, 5), ranks=(4, 8, 16), alphas=(8.0, 16.0, 32.0), d_in=64, d_out=32, dtype="bf16", T=None):
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return P.Desc(off, ranks, alphas, d_in, d_out, dtype, T)
+
+
+def test_validation_codes(P):
+    assert P.plora_validate(desc(P)) == 0
+    assert P.plora_validate(desc(P, d_in=12)) == -5
+    assert P.plora_validate(desc(P, d_out=0)) == -5
+    assert P.plora_validate(desc(P, ranks=(4, 0, 16))) == -3
+    assert P.plora_validate(desc(P, ranks=(4, 129, 16))) == -3
+    assert P.plora_validate(desc(P, alphas=(8.0, float("inf"), 1.0))) == -4
+    assert P.plora_validate(desc(P, T=9)) == -2
+    d = desc(P)
+    d.offsets[1] = 5  # 0, 5, 3, 8: decreasing
+    assert P.plora_validate(d) == -2
+    d = desc(P)
+    d.c.dtype = 7
+    assert P.plora_validate(d) == -7
+    d = desc(P)
+    d.c.n_adapters = 65
+    assert P.plora_validate(d) == -6
+    # no adapters: any token count, offsets unused
+    d0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=17)
+    assert P.plora_validate(d0) == 0
+
+
+def test_sizes(P):
+    d = desc(P, counts=(3, 0, 5), ranks=(4, 8, 16))
+    assert P.plora_h_elems(d) == 3 * 4 + 0 + 5 * 16
+    # small adapters fit one token chunk: no partials
+    assert P.plora_workspace_bytes(d) == 0
+    big = desc(P, counts=(5000, 1, 0), ranks=(64, 8, 16), d_in=4096, d_out=16384)
+    # d_in <= 8192: 1024-token chunks; d_out > 8192: 2048-token chunks; only adapter 0 is split
+    a = 5 * 64 * 4096 * 4
+    b = 3 * 64 * 16384 * 4
+    assert P.plora_workspace_bytes(big) == ((a + 255) // 256) * 256 + ((b + 255) // 256) * 256
+    assert P.plora_workspace_bytes(desc(P, d_in=12)) == 0  # invalid -> 0
+    assert P.plora_workspace_bytes(desc(P, dtype="f32")) == 0
+
+
+def raw(lib_fn_name, P, *args):
+    return getattr(P._lib, lib_fn_name)(*args)
+
+
+def test_error_paths_have_no_side_effects(P):
+    d = desc(P)
+    # NULL required pointers
+    rc = P._lib.plora_forward(d.ref(), None, None, None, None, None, None, None)
+    assert rc == -1 and "required" in P.plora_last_error()
+    # misaligned device pointers are rejected before any launch
+    rc = P._lib.plora_forward(d.ref(), 0x1001, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None)
+    assert rc == -9
+    rc = P._lib.plora_backward_dx(d.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5008, 0x6000, None)
+    assert rc == -9
+    # invalid descriptor
+    bad = desc(P, ranks=(4, 0, 16))
+    assert P._lib.plora_backward_dAdB(bad.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0,
+                                      None) == -3
+    # workspace too small
+    big = desc(P, counts=(5000, 1, 0), ranks=(64, 8, 16), d_in=4096, d_out=16384)
+    rc = P._lib.plora_backward_dAdB(big.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 16, None)
+    assert rc == -8 and "workspace" in P.plora_last_error()
+    # T = 0 forward is a no-op (nothing touched, no GPU needed)
+    z = P.Desc([0, 0, 0], [4, 8], [1.0, 1.0], 64, 32, "bf16")
+    assert P._lib.plora_forward(z.ref(), None, None, None, None, None, None, None) == 0
+    assert P._lib.plora_backward_dx(z.ref(), None, None, None, None, None, None, None) == 0
+    # N = 0 backward_dAdB is a no-op
+    n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
+    assert P._lib.plora_backward_dAdB(n0.ref(), None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_python_shape_checks(P):
+    torch = pytest.importorskip("torch")
+    d = desc(P, counts=(3, 0, 5), d_in=64, d_out=32)
+    X = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        P.plora_forward(d, X, torch.zeros(32, 65, dtype=torch.bfloat16), None, None, None, None, stream=0)
+    with pytest.raises(ValueError):
+        P.plora_forward(d, X.float(), None, None, None, None, None, stream=0)
+
+
+def test_profile_read_empty(P):
+    P.plora_profile_reset()
+    assert P.plora_profile_read("gemm_fwd") == (0, 0.0)
+
+
+def test_planner_host_only_build(tmp_path):
+    """The planner is plain C++: it builds with g++ alone and its tables are checked here."""
+    src = os.path.join(ROOT, "packed_adapter_lora_amd", "csrc", "plan.cpp")
+    drv = tmp_path / "drv.cpp"
+    drv.write_text(r'''
+#include "plan.h"
+#include <cstdio>
+int main() {
+  int64_t off[5] = {0, 70, 70, 71, 4171};
+  int32_t rk[4] = {8, 16, 3, 64};
+  float al[4] = {16.f, 16.f, 6.f, 32.f};
+  plora_desc d{4, PLORA_BF16, 4171, 4096, 14336, off, rk, al};
+  const char* why;
+  if (plora::validate_desc(&d, &why)) return 1;
+  plora::SegTable s; plora::build_segtable(&d, &s);
+  plora::WorkMap m; int u = plora::build_shrink_map(s, &m);
+  plora::WgradPlan pa, pb; plora::build_wgrad_plan(s, 4096, &pa); plora::build_wgrad_plan(s, 14336, &pb);
+  std::printf("%d %d %d %d %d %lld %lld %d %d %lld %d %g %g\n", u, m.pre[1], m.pre[2], m.pre[3], s.roff[4],
+              (long long)s.hoff[4], (long long)pa.part_elems, pa.chunks.pre[4], pb.chunks.pre[4],
+              (long long)pb.part_elems, s.rmax, s.scale[0], s.scale[2]);
+  return 0;
+}
+''')
+    exe = tmp_path / "drv"
+    import subprocess
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", os.path.join(ROOT, "include"), "-I",
+                    os.path.join(ROOT, "packed_adapter_lora_amd", "csrc"), str(drv), src, "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], stdout=subprocess.PIPE, text=True, check=True).stdout.split()
+    # shrink tiles of 32 rows: 3 + 0 + 1 + 129
+    assert out[:4] == ["133", "3", "3", "4"]
+    assert out[4] == "91"  # R
+    assert out[5] == str(70 * 8 + 1 * 3 + 4100 * 64)
+    # dA (1024-token chunks): adapter 3 has 5 chunks -> partials 5*64*4096
+    assert out[6] == str(5 * 64 * 4096) and out[7] == str(1 + 0 + 1 + 5)
+    # dB (2048-token chunks): adapter 3 has 3 chunks
+    assert out[8] == str(1 + 0 + 1 + 3) and out[9] == str(3 * 64 * 14336)
+    assert out[10] == "64" and float(out[11]) == 2.0 and float(out[12]) == 2.0
