@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the packed multi-LoRA operator, forward + backward, on one MI355X.
+
+One step = plora_forward + plora_backward_dx + plora_backward_dAdB over one
+batch of synthetic inputs already resident in HBM.  Default workload: the
+Llama-3-8B-shaped up projection 4096 -> 14336, bf16, 32 adapters with ranks
+cycling 8/16/32/64 and alpha 8/16/32, 2048 tokens each (T = 65536).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama_up]
+                    [--adapters 32] [--no-cpu] [--sweep]
+
+Prints one JSON line.  ``roofline`` describes the dominant kernel (the base
+GEMM with the fused LoRA expand): algorithmic FLOPs per launch over its mean
+duration, measured with HIP events recorded by the library on the stream it
+launches on.  ``cpu_baseline`` times the fp64 oracle on the host on a bounded
+token sample of the same workload.  ``--sweep`` adds one line per adapter
+count (2..32, 2048 tokens each) for the scaling curve.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gemm_flops(wl, which):
+    """Algorithmic FLOPs of one launch of the base GEMM with its fused expand."""
+    nr = float(np.sum(np.diff(wl.offsets) * wl.ranks)) if wl.n_adapters else 0.0
+    base = 2.0 * wl.T * wl.d_in * wl.d_out
+    return base + 2.0 * nr * (wl.d_out if which == "gemm_fwd" else wl.d_in)
+
+
+def step_flops(wl):
+    nr = float(np.sum(np.diff(wl.offsets) * wl.ranks)) if wl.n_adapters else 0.0
+    return 4.0 * wl.T * wl.d_in * wl.d_out + 6.0 * nr * (wl.d_in + wl.d_out)
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel, wl):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel; else None."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        rec = json.load(open(f)).get(kernel)
+    except ValueError:
+        return None
+    if not rec or rec.get("workload") != wl.name or rec.get("tokens") != wl.T:
+        return None
+    src = os.path.join(ROOT, "packed_adapter_lora_amd", "csrc", rec.get("source", ""))
+    if not os.path.exists(src) or source_sha(src) != rec.get("source_sha"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_device_inputs(wl):
+    import torch
+    import workloads
+    inp = workloads.make_inputs(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = {k: torch.from_numpy(v).to("cuda").to(dt) for k, v in inp.items()}
+    return inp, dev
+
+
+def run_bench(wl, steps, warmup):
+    import torch
+    import packed_adapter_lora_amd as P
+    inp, dev = make_device_inputs(wl)
+    d = P.Desc.from_workload(wl)
+    he = P.plora_h_elems(d)
+    dt = dev["X"].dtype
+    Y = torch.empty((wl.T, wl.d_out), dtype=dt, device="cuda")
+    dX = torch.empty((wl.T, wl.d_in), dtype=dt, device="cuda")
+    H = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he]
+    G = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he]
+    dA = torch.empty((wl.R, wl.d_in), dtype=torch.float32, device="cuda")
+    dB = torch.empty((wl.R, wl.d_out), dtype=torch.float32, device="cuda")
+    nb = P.plora_workspace_bytes(d)
+    ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        P.plora_forward(d, dev["X"], dev["W"], dev["A"], dev["B"], Y, H, stream)
+        P.plora_backward_dx(d, dev["dY"], dev["W"], dev["A"], dev["B"], dX, G, stream)
+        P.plora_backward_dAdB(d, dev["X"], dev["dY"], H, G, dA, dB, ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    P.plora_profile_reset()
+    P.plora_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    P.plora_profile_enable(False)
+    kern = {}
+    for cls in ("shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce"):
+        n, ms = P.plora_profile_read(cls)
+        kern[cls] = {"launches": n, "mean_ms": (ms / n) if n else 0.0, "ms_per_step": ms / steps}
+    P.plora_profile_reset()
+    del Y, dX, H, G, dA, dB, ws, dev
+    torch.cuda.empty_cache()
+    return (t1 - t0) / steps, kern, inp
+
+
+def cpu_baseline(wl, inp, per_segment):
+    """fp64 oracle on the first `per_segment` tokens of every segment: Y, H, dX,
+    G and dA/dB over those tokens, as the oracle stands."""
+    import oracle
+    rows = []
+    for i in range(wl.n_adapters):
+        a, b = int(wl.offsets[i]), int(wl.offsets[i + 1])
+        rows.extend(range(a, min(b, a + per_segment)))
+    rows = np.array(rows, dtype=np.int64)
+    seg = np.searchsorted(wl.offsets, rows, side="right") - 1
+    counts = np.bincount(seg, minlength=wl.n_adapters)
+    sub_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    X, dY = inp["X"][rows].astype(np.float64), inp["dY"][rows].astype(np.float64)
+    W, A, B = (inp[k].astype(np.float64) for k in ("W", "A", "B"))
+    t0 = time.perf_counter()
+    oracle.packed_lora(sub_off, wl.ranks, wl.alphas.astype(np.float64), wl.d_in, wl.d_out, X=X, dY=dY, W=W, A=A,
+                       B=B, want=("Y", "H", "dX", "G", "dA", "dB"))
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "first %d tokens of each of the %d segments (%d tokens), full d_in x d_out, all of Y, H, dX, "
+                      "G, dA, dB over them; %.1f s" % (per_segment, wl.n_adapters, len(rows), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama_up")
+    ap.add_argument("--adapters", type=int, default=None)
+    ap.add_argument("--cpu-tokens", type=int, default=8, help="oracle sample: tokens per segment")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the packed-LoRA operator here has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+        return
+
+    wl = workloads.config(args.workload, n_adapters=args.adapters)
+    log("workload %s: T=%d d_in=%d d_out=%d N=%d R=%d" % (wl.name, wl.T, wl.d_in, wl.d_out, wl.n_adapters, wl.R))
+    sec, kern, inp = run_bench(wl, args.steps, args.warmup)
+    tokens_per_s = wl.T / sec
+    dom = max(("gemm_fwd", "gemm_bwd"), key=lambda k: kern[k]["mean_ms"])
+    flops = gemm_flops(wl, dom)
+    achieved = flops / (kern[dom]["mean_ms"] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, wl), "kernel": dom,
+            "flops_per_launch": flops, "mean_launch_ms": round(kern[dom]["mean_ms"], 4)}
+    whole = step_flops(wl) / sec / 1e12
+    cpu = None
+    if not args.no_cpu:
+        log("timing the oracle on the host ...")
+        cpu = cpu_baseline(wl, inp, args.cpu_tokens)
+    out = {
+        "metric": "packed LoRA fwd+bwd tokens/sec at %d adapters" % wl.n_adapters,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal draws; no dataset or checkpoint)",
+        "config": {"workload": "llama3_8b_%s_%dx%d_%d_adapters_x_%d_tokens" % (
+            wl.name, wl.d_in, wl.d_out, wl.n_adapters, int(wl.counts.max())) if wl.n_adapters else wl.name,
+            "d_in": wl.d_in, "d_out": wl.d_out, "n_adapters": wl.n_adapters, "tokens": wl.T,
+            "ranks": sorted(set(wl.ranks.tolist())), "sum_ranks": wl.R},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "whole_step_tflops": round(whole, 1),
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kern.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+    if args.sweep:
+        for n in (2, 4, 8, 16, 32):
+            w2 = workloads.config(args.workload, n_adapters=n)
+            s2, k2, _ = run_bench(w2, args.steps, args.warmup)
+            print(json.dumps({"sweep": True, "workload": w2.name, "n_adapters": n, "tokens": w2.T,
+                              "tokens_per_s": round(w2.T / s2, 1), "ms_per_step": round(s2 * 1e3, 4),
+                              "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in k2.items()}}),
+                  flush=True)
+
+
+if __name__ == "__main__":
+    main()

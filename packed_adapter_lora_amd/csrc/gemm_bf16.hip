@@ -65,6 +65,145 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_q, int tiles
     tp = in / gsize;
 }
 
+
+// Fragment of a p-contiguous tile: 8 consecutive k of feature p, read
+// transposed from rows k..k+7 (2 bytes per lane per row).
+__device__ __forceinline__ bf16x8 pfrag_rows(const uint8_t* base, int row_bytes, int p, int k) {
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const uint16_t*>(base + (k + e) * row_bytes + p * 2);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// LoRA expand appended to the K loop of one 256 x 256 tile: for every adapter
+// whose segment overlaps the tile's tokens, K = r_i more MFMA steps with
+// A = E rows (B_i or A_i^T, p-contiguous) and B = s_i * F_i split into bf16
+// hi + lo, zero outside the segment.  se: >= 64 rows of se_row bytes;
+// shi/slo: 32 KiB K-contiguous tiles.  Must be called by the whole workgroup
+// once the LDS used by the K loop is free.
+__device__ __forceinline__ void lora_expand(f32x16 (&acc)[4][4], const GemmArgs& a, const SegTable& seg,
+                                            int64_t q0, int64_t p0, uint8_t* se, int se_row, uint8_t* shi,
+                                            uint8_t* slo) {
+    const bf16* __restrict__ E = static_cast<const bf16*>(a.E);
+    const float* __restrict__ F = a.F;
+    const int64_t T = a.T, Pdim = a.Pdim;
+    const int tid = (int)threadIdx.x, l = lane_id(), w = wave_id();
+    const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+    const int64_t tq1 = q0 + kBQ < T ? q0 + kBQ : T;
+    for (int i = segment_of(seg, q0); i < seg.n && seg.off[i] < tq1; ++i) {
+        const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
+        if (s1 <= s0 || s1 <= q0) continue;
+        const int r = seg.rank[i];
+        const float sc = seg.scale[i];
+        const int64_t rbase = seg.roff[i];
+        const float* Fi = F + seg.hoff[i];
+        for (int jb = 0; jb < r; jb += 64) {
+            const int rc = r - jb < 64 ? r - jb : 64;
+            const int nkk = (rc + 15) >> 4;
+            // issue every global load of this chunk before touching LDS: one
+            // round trip.  E: 16*nkk rows x 32 chunks of 16 B (8 per thread at
+            // most); F: thread tid owns token row q0 + tid (rc fp32 values).
+            u32x4 ev[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int id = tid + u * kThreads;
+                const int j = id >> 5, pc = id & 31;
+                const int64_t p = p0 + pc * 8;
+                ev[u] = load16_or_zero(E + (rbase + jb + j) * Pdim + p, j < rc && p < Pdim);
+            }
+            const int64_t t = q0 + tid;
+            const bool in = t >= s0 && t < s1;
+            const float* frow = Fi + (in ? (t - s0) * r + jb : 0);
+            float fv[64];
+            if (((seg.hoff[i] + jb) & 3) == 0 && (r & 3) == 0) {
+                // rows start on 16-byte boundaries: 4 values per load (rc is a multiple of 4)
+#pragma unroll
+                for (int j4 = 0; j4 < 16; ++j4) {
+                    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                    if (in && 4 * j4 < rc) v = *reinterpret_cast<const f32x4*>(frow + 4 * j4);
+                    fv[4 * j4 + 0] = v[0];
+                    fv[4 * j4 + 1] = v[1];
+                    fv[4 * j4 + 2] = v[2];
+                    fv[4 * j4 + 3] = v[3];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 64; ++j) fv[j] = (in && j < rc) ? frow[j] : 0.0f;
+            }
+            __syncthreads();  // the K loop / previous chunk is done with LDS
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int id = tid + u * kThreads;
+                const int j = id >> 5, pc = id & 31;
+                if (j < 16 * nkk) *reinterpret_cast<u32x4*>(se + j * se_row + pc * 16) = ev[u];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (c >= 2 * nkk) break;
+                u16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bf16 h, o;
+                    split_bf16(sc * fv[c * 8 + e], h, o);
+                    hi[e] = __builtin_bit_cast(uint16_t, h);
+                    lo[e] = __builtin_bit_cast(uint16_t, o);
+                }
+                *reinterpret_cast<u16x8*>(shi + kmaj(tid, c)) = hi;
+                *reinterpret_cast<u16x8*>(slo + kmaj(tid, c)) = lo;
+            }
+            __syncthreads();
+            for (int kk = 0; kk < nkk; ++kk) {
+                bf16x8 fa[4], fh[4], fl[4];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    fa[mt] = pfrag_rows(se, se_row, wp * 128 + mt * 32 + l32, 16 * kk + 8 * lh);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int row = wq * 128 + nt * 32 + l32;
+                    fh[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(shi + kmaj(row, 2 * kk + lh)));
+                    fl[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(slo + kmaj(row, 2 * kk + lh)));
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        acc[mt][nt] = mfma32x32x16(fa[mt], fh[nt], acc[mt][nt]);
+                        acc[mt][nt] = mfma32x32x16(fa[mt], fl[nt], acc[mt][nt]);
+                    }
+            }
+        }
+    }
+}
+
+// One rounding to bf16, token-major stores: lane holds features
+// p .. p+3 (p = 8*(v/4) + 4*(l/32)) of token q = l%32 in each 32 x 32 block.
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const GemmArgs& a, int64_t q0, int64_t p0) {
+    bf16* __restrict__ O = static_cast<bf16*>(a.O);
+    const int64_t T = a.T, Pdim = a.Pdim;
+    const int l = lane_id(), w = wave_id();
+    const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int64_t t = q0 + wq * 128 + nt * 32 + l32;
+        if (t >= T) continue;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t p = p0 + wp * 128 + mt * 32 + 8 * g + 4 * lh;
+                if (p < Pdim) {
+                    bf16x4 o;
+                    o[0] = to_bf16(acc[mt][nt][4 * g + 0]);
+                    o[1] = to_bf16(acc[mt][nt][4 * g + 1]);
+                    o[2] = to_bf16(acc[mt][nt][4 * g + 2]);
+                    o[3] = to_bf16(acc[mt][nt][4 * g + 3]);
+                    *reinterpret_cast<bf16x4*>(O + t * Pdim + p) = o;
+                }
+            }
+        }
+    }
+}
+
 template <bool P_KMAJOR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTable seg) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
@@ -178,96 +317,201 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTab
         __syncthreads();
     }
 
-    // ---- LoRA expand: K = r_i more steps per overlapping adapter -------------
-    if (a.lora && seg.n > 0) {
-        const bf16* __restrict__ E = static_cast<const bf16*>(a.E);
-        const float* __restrict__ F = a.F;
-        const int64_t tq1 = q0 + kBQ < T ? q0 + kBQ : T;
-        uint8_t* se = smem;                 // [j][p] p-contiguous, up to 64 rows
-        uint8_t* shi = smem + kPTile;       // [q][j] K-contiguous (hi terms)
-        uint8_t* slo = shi + kKTile;        // [q][j] K-contiguous (lo terms)
-        for (int i = segment_of(seg, q0); i < seg.n && seg.off[i] < tq1; ++i) {
-            const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
-            if (s1 <= s0 || s1 <= q0) continue;
-            const int r = seg.rank[i];
-            const float sc = seg.scale[i];
-            const int64_t rbase = seg.roff[i];
-            const float* Fi = F + seg.hoff[i];
-            for (int jb = 0; jb < r; jb += 64) {
-                const int rc = r - jb < 64 ? r - jb : 64;
-                const int nkk = (rc + 15) >> 4;
-                __syncthreads();
-                for (int id = tid; id < 16 * nkk * 32; id += kThreads) {
-                    const int j = id >> 5, pc = id & 31;
-                    const int64_t p = p0 + pc * 8;
-                    *reinterpret_cast<u32x4*>(se + j * kPRow + pc * 16) =
-                        load16_or_zero(E + (rbase + jb + j) * Pdim + p, j < rc && p < Pdim);
-                }
-                const int nch = 2 * nkk;
-                for (int id = tid; id < kBQ * nch; id += kThreads) {
-                    const int q = id / nch, c = id - q * nch;
-                    const int64_t t = q0 + q;
-                    const bool in = t >= s0 && t < s1;
-                    u16x8 hi, lo;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int j = c * 8 + e;
-                        const float v = (in && j < rc) ? sc * Fi[(t - s0) * r + jb + j] : 0.0f;
-                        bf16 h, o;
-                        split_bf16(v, h, o);
-                        hi[e] = __builtin_bit_cast(uint16_t, h);
-                        lo[e] = __builtin_bit_cast(uint16_t, o);
-                    }
-                    *reinterpret_cast<u16x8*>(shi + kmaj(q, c)) = hi;
-                    *reinterpret_cast<u16x8*>(slo + kmaj(q, c)) = lo;
-                }
-                __syncthreads();
-                for (int kk = 0; kk < nkk; ++kk) {
-                    bf16x8 fa[4], fh[4], fl[4];
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) fa[mt] = pfrag_t(se, wp * 128 + mt * 32 + l32, 16 * kk + 8 * lh);
-#pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
-                        const int row = wq * 128 + nt * 32 + l32;
-                        fh[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(shi + kmaj(row, 2 * kk + lh)));
-                        fl[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(slo + kmaj(row, 2 * kk + lh)));
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int nt = 0; nt < 4; ++nt) {
-                            acc[mt][nt] = mfma32x32x16(fa[mt], fh[nt], acc[mt][nt]);
-                            acc[mt][nt] = mfma32x32x16(fa[mt], fl[nt], acc[mt][nt]);
-                        }
-                }
-            }
-        }
-    }
-
-    // ---- one rounding to bf16, token-major stores ----------------------------
-    bf16* __restrict__ O = static_cast<bf16*>(a.O);
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int64_t t = q0 + wq * 128 + nt * 32 + l32;
-        if (t >= T) continue;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t p = p0 + wp * 128 + mt * 32 + 8 * g + 4 * lh;
-                if (p < Pdim) {
-                    bf16x4 o;
-                    o[0] = to_bf16(acc[mt][nt][4 * g + 0]);
-                    o[1] = to_bf16(acc[mt][nt][4 * g + 1]);
-                    o[2] = to_bf16(acc[mt][nt][4 * g + 2]);
-                    o[3] = to_bf16(acc[mt][nt][4 * g + 3]);
-                    *reinterpret_cast<bf16x4*>(O + t * Pdim + p) = o;
-                }
-            }
-        }
-    }
+    // ---- LoRA expand, then one rounding to bf16 -------------------------------
+    if (a.lora && seg.n > 0) lora_expand(acc, a, seg, q0, p0, smem, kPRow, smem + kPTile, smem + kPTile + kKTile);
+    store_tile(acc, a, q0, p0);
 }
 
+
+// ===========================================================================
+// Pipelined forward kernel (K-contiguous weight, K a multiple of 128).
+//
+// Global -> LDS without registers: buffer_load_dwordx4 ... lds (gfx950 LDS
+// DMA, 16 bytes per lane, 1 KiB per instruction = 8 rows x 128 bytes, i.e.
+// whole cache lines).  Two LDS stages of BK = 64 (64 KiB each: weight tile
+// then token tile, 128-byte rows, XOR-swizzled 16-byte chunks); each stage
+// buffer is its own __shared__ array so the compiler can tell which LDS DMA a
+// fragment read depends on.  Rows past the tensor's end fall outside the
+// buffer resource's range and read as zero.  Per stage: four k16 steps of 16
+// MFMAs per wave; the fragments of step s+1 are read while step s runs; one
+// barrier per stage, before the last step, after which the freed buffer is
+// refilled with stage k+2 while the last step runs.
+// ===========================================================================
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kPipeTile = 256 * kKRow;           // 32 KiB: 256 rows x 128 B
+constexpr int kPipeStage = 2 * kPipeTile;        // 64 KiB
+constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data format (gfx9 family)
+#ifndef PLORA_DMA_SPLIT
+#define PLORA_DMA_SPLIT 8                         // of a stage's 16 loads per wave, issued one step later
+#endif
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kPipeStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kPipeStage];
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// workgroup barrier for LDS only: wait for this wave's LDS reads, then s_barrier
+// (no vmcnt drain, so in-flight prefetches stay in flight)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// p-contiguous weight tile (backward): 64 k-rows x 512 B; the 16-byte chunk c of
+// row k is stored at chunk c ^ 4*(k%4), so the 16 lanes of a transposed read
+// (4 rows x 32 bytes) and the next 16 (the next 32 bytes) hit distinct banks.
+__device__ __forceinline__ int tofs(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
+
+typedef __bf16 bf16x4v __attribute__((vector_size(8)));
+
+// 8 consecutive k of feature p from a p-contiguous tile with two transposed
+// LDS reads (ds_read_b64_tr_b16).  Within each 16-lane group, lane L supplies
+// the address of k-row kb + L/4, features pc + 4*(L%4) .. +3, and lane i gets
+// back rows kb..kb+3 of feature pc + i.
+__device__ __forceinline__ bf16x8 pfrag_tr(const uint8_t* tile, int prow0, int kb) {
+    const int l = lane_id(), L = l & 15, g = l >> 4;
+    const int p = prow0 + 16 * (g & 1) + 4 * (L & 3);
+    const int k = kb + 8 * (g >> 1) + (L >> 2);
+    const uint8_t* a0 = tile + tofs(k, p >> 3) + (p & 7) * 2;
+    const uint8_t* a1 = tile + tofs(k + 4, p >> 3) + (p & 7) * 2;
+    typedef __attribute__((address_space(3))) bf16x4v lds_v4;
+    const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a0));
+    const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+template <bool P_KMAJOR>
+__global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, SegTable seg) {
+    const int64_t T = a.T, K = a.K, Pdim = a.Pdim;
+    const int tiles_q = (int)((T + kBQ - 1) / kBQ);
+    const int tiles_p = (int)((Pdim + kBP - 1) / kBP);
+    int tq, tp;
+    tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, tq, tp);
+    const int64_t q0 = (int64_t)tq * kBQ, p0 = (int64_t)tp * kBP;
+    const int l = lane_id(), w = wave_id();
+    const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+
+    const int64_t prow = Pdim - p0 < kBP ? Pdim - p0 : kBP;
+    const int64_t qrow = T - q0 < kBQ ? T - q0 : kBQ;
+    // weight tile: K-contiguous rows p0.. (forward) or p-contiguous rows k.. of
+    // columns p0.. (backward; columns past Pdim read neighbouring data that only
+    // feeds output columns that are never stored)
+    const __amdgpu_buffer_rsrc_t rp =
+        P_KMAJOR ? __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const bf16*>(a.P) + p0 * K), 0,
+                                                     (int)(prow * K * 2), kRsrcWord3)
+                 : __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<const bf16*>(a.P) + p0), 0,
+                                                     (int)((K * Pdim - p0) * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.Q) + q0 * K), 0, (int)(qrow * K * 2), kRsrcWord3);
+    // LDS DMA block b (1 KiB).  K-contiguous tiles: 8 rows x 128 B, lane l fills
+    // row 8b + l/8, physical chunk l%8.  p-contiguous tile: 2 k-rows x 512 B, lane
+    // l fills k-row 2b + l/32, physical chunk l%32.  Wave w owns blocks 8w..8w+7.
+    // (row = 8b + l/8, so its swizzle (row ^ row/8) % 8 = (l/8 ^ b) % 8 = (l/8 ^ j) % 8)
+    const int r0 = l >> 3;
+    const uint32_t lane_row = (uint32_t)(r0 * K * 2);
+    const uint32_t blk_stride = (uint32_t)(8 * K * 2);  // 8 rows
+    // (row k = 2b + l/32, so k%4 = 2*(b%2) + l/32: one lane offset per block parity)
+    const int tr = l >> 5;
+    const uint32_t lane_off_t0 = (uint32_t)(tr * Pdim * 2) + (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
+    const uint32_t lane_off_t1 = (uint32_t)(tr * Pdim * 2) + (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
+    const uint32_t blk_stride_t = (uint32_t)(2 * Pdim * 2);  // 2 k-rows
+    const int KT = (int)(K / 64);
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: LDS DMA bases stay scalar
+    // loads j0 .. j1-1 of this wave's 16 for stage kt (0..7: weight tile, 8..15: token tile)
+    auto issue = [&](uint8_t* buf, int kt, int j0, int j1) {
+        // past the last stage: push the offset beyond the resource's range (all
+        // ranges are < 2^31 bytes), so the load writes zeros; no branch
+        const uint32_t oob = kt < KT ? 0u : 0x80000000u;
+        const uint32_t kb = (uint32_t)kt * 128u + oob;
+        const uint32_t kbt = (uint32_t)kt * (uint32_t)(64 * Pdim * 2) + oob;
+#pragma unroll
+        for (int j = j0; j < j1; ++j) {
+            const int blk = 8 * wu + (j & 7);
+            uint32_t vo;
+            if (!P_KMAJOR && j < 8)
+                vo = ((j & 1) ? lane_off_t1 : lane_off_t0) + (uint32_t)blk * blk_stride_t + kbt;
+            else
+                vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ j) & 7)) << 4) + (uint32_t)blk * blk_stride + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 8 ? rp : rq,
+                                                     (lds_void*)(buf + (j < 8 ? 0 : kPipeTile) + blk * 1024), 16, vo,
+                                                     0, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    bf16x8 fa[2][4], fb[2][4];
+    auto rd = [&](const uint8_t* buf, int kk, int s) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            if constexpr (P_KMAJOR)
+                fa[s][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kmaj(wp * 128 + m * 32 + l32, 2 * kk + lh)));
+            else
+                fa[s][m] = pfrag_tr(buf, wp * 128 + m * 32, 16 * kk);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            fb[s][n] = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(buf + kPipeTile + kmaj(wq * 128 + n * 32 + l32, 2 * kk + lh)));
+    };
+    auto mm = [&](int s) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[m][n] = mfma32x32x16(fa[s][m], fb[s][n], acc[m][n]);
+    };
+    // 16 MFMAs interleaved with 8 fragment reads (and `dma` LDS DMA loads)
+    auto sched = [&](int dma) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // LDS DMA load
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (i + 8 < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    constexpr int kLate = PLORA_DMA_SPLIT;  // loads of stage kt+1 issued during step 0 of stage kt
+    // stage kt in `cur`, stage kt+1 landing in `nxt`
+    auto stage = [&](uint8_t* cur, uint8_t* nxt, int kt) {
+        issue(nxt, kt + 1, 16 - kLate, 16);
+        rd(cur, 1, 1);
+        mm(0);
+        sched(kLate);
+        rd(cur, 2, 0);
+        mm(1);
+        sched(0);
+        rd(cur, 3, 1);
+        mm(0);
+        sched(0);
+        wait_vmcnt<0>();  // stage kt+1 landed
+        lds_barrier();    // and every wave is done reading `cur`
+        __builtin_amdgcn_sched_barrier(0);
+        issue(cur, kt + 2, 0, 16 - kLate);
+        rd(nxt, 0, 0);
+        mm(1);
+        sched(16 - kLate);
+    };
+
+    issue(g_stage0, 0, 0, 16);
+    issue(g_stage1, 1, 0, 16 - kLate);
+    wait_vmcnt<16 - kLate>();
+    lds_barrier();
+    rd(g_stage0, 0, 0);
+    for (int kt = 0; kt < KT; kt += 2) {  // KT is even
+        stage(g_stage0, g_stage1, kt);
+        stage(g_stage1, g_stage0, kt + 1);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+
+    if (a.lora && seg.n > 0) lora_expand(acc, a, seg, q0, p0, g_stage0, kBP * 2, g_stage0 + kPipeTile, g_stage1);
+    store_tile(acc, a, q0, p0);
+}
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st) {
@@ -276,7 +520,13 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg), block(kThreads);
-    if (p_kmajor)
+    const bool pipelined = a.K % 128 == 0 && a.K <= (int64_t(1) << 22) && a.Pdim <= (int64_t(1) << 22) &&
+                           a.K * a.Pdim * 2 < (int64_t(1) << 31);
+    if (pipelined && p_kmajor)
+        hipLaunchKernelGGL(gemm_lora_bf16_pipe<true>, grid, block, 0, st, a, s);
+    else if (pipelined)
+        hipLaunchKernelGGL(gemm_lora_bf16_pipe<false>, grid, block, 0, st, a, s);
+    else if (p_kmajor)
         hipLaunchKernelGGL(gemm_lora_bf16<true>, grid, block, 0, st, a, s);
     else
         hipLaunchKernelGGL(gemm_lora_bf16<false>, grid, block, 0, st, a, s);
