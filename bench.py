@@ -73,6 +73,75 @@ def load_traffic(kernel, wl):
     return rec.get("bytes_per_launch")
 
 
+KERNEL_CLASSES = (("gemm_lora_bf16_pipe<true>", "gemm_fwd"), ("gemm_lora_bf16_pipe<false>", "gemm_bwd"),
+                  ("gemm_lora_bf16<true>", "gemm_fwd"), ("gemm_lora_bf16<false>", "gemm_bwd"),
+                  ("shrink_bf16", "shrink"), ("wgrad_reduce", "reduce"), ("wgrad_bf16", "wgrad"))
+
+
+def kernel_class(name):
+    for key, cls in KERNEL_CLASSES:
+        if key in name:
+            return cls
+    return None
+
+
+def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, workload, cmds):
+    """Summaries of rocprofv3 csv output: per-kernel time (--kernel-trace --stats) and
+    HBM bytes per launch (FETCH_SIZE / WRITE_SIZE), each counter scaled by what it
+    reads for a plain device copy of known size."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        f = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+        return list(csv.DictReader(open(f[0]))) if f else []
+
+    out = {}
+    stats = rows(trace_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics, workload %s" % workload, "# command: " + cmds["trace"], "",
+             "%-16s %6s %12s %12s  %s" % ("class", "calls", "total_ms", "avg_us", "kernel")]
+    for r in stats:
+        cls = kernel_class(r["Name"]) or "-"
+        lines.append("%-16s %6s %12.3f %12.1f  %s" % (cls, r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+                                                       float(r["AverageNs"]) / 1e3, r["Name"][:110]))
+    out["stats"] = "\n".join(lines) + "\n"
+
+    def counter(d, cname):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return acc
+
+    cf, cw = counter(copy_fetch_dir, "FETCH_SIZE"), counter(copy_write_dir, "WRITE_SIZE")
+    copy_name = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
+    kib = copy_bytes / 1024.0
+    f_scale = kib / max(v for k in copy_name for v in cf[k])
+    w_scale = kib / max(v for k in copy_name if k in cw for v in cw[k])
+    fetch, write = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    lines = ["# HBM traffic per launch from rocprofv3 counters, workload %s" % workload,
+             "# fetch: " + cmds["fetch"], "# write: " + cmds["write"],
+             "# copy calibration (%d bytes): %s ; %s" % (copy_bytes, cmds["copy_fetch"], cmds["copy_write"]),
+             "# scale: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f (counter KiB -> bytes moved by a plain copy)" % (
+                 f_scale, w_scale), "",
+             "%-10s %6s %16s %16s %14s" % ("class", "disp", "fetch_MiB", "write_MiB", "total_MiB")]
+    traffic = {}
+    for name in sorted(set(fetch) | set(write)):
+        cls = kernel_class(name)
+        if not cls:
+            continue
+        fv = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [0]))) * f_scale * 1024
+        wv = sum(write.get(name, [0])) / max(1, len(write.get(name, [0]))) * w_scale * 1024
+        lines.append("%-10s %6d %16.1f %16.1f %14.1f" % (cls, len(fetch.get(name, [])), fv / 2 ** 20, wv / 2 ** 20,
+                                                          (fv + wv) / 2 ** 20))
+        traffic[cls] = {"fetch_bytes": fv, "write_bytes": wv, "bytes_per_launch": fv + wv, "kernel": name}
+    out["traffic_txt"] = "\n".join(lines) + "\n"
+    out["traffic"] = traffic
+    out["scales"] = (f_scale, w_scale)
+    return out
+
+
 def make_device_inputs(wl):
     import torch
     import workloads
@@ -149,6 +218,31 @@ def cpu_baseline(wl, inp, per_segment):
                       "G, dA, dB over them; %.1f s" % (per_segment, wl.n_adapters, len(rows), dt)}
 
 
+def write_profiles(d, workload):
+    import workloads
+    wl = workloads.config(workload)
+    cmds = json.load(open(os.path.join(d, "commands.json")))
+    res = rocprof_summary(os.path.join(d, "trace"), os.path.join(d, "fetch"), os.path.join(d, "write"),
+                          os.path.join(d, "copy_fetch"), os.path.join(d, "copy_write"), cmds["copy_bytes"],
+                          wl.name, cmds)
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    open(os.path.join(prof, "kernels_%s_stats.txt" % wl.name), "w").write(res["stats"])
+    open(os.path.join(prof, "kernels_%s_hbm_traffic.txt" % wl.name), "w").write(res["traffic_txt"])
+    src = {"gemm_fwd": "gemm_bf16.hip", "gemm_bwd": "gemm_bf16.hip", "shrink": "lora_bf16.hip",
+           "wgrad": "lora_bf16.hip", "reduce": "lora_bf16.hip"}
+    tj = {}
+    for cls, rec in res["traffic"].items():
+        f = os.path.join(ROOT, "packed_adapter_lora_amd", "csrc", src[cls])
+        tj[cls] = {"workload": wl.name, "tokens": wl.T, "source": src[cls], "source_sha": source_sha(f),
+                   "bytes_per_launch": round(rec["bytes_per_launch"]), "fetch_bytes": round(rec["fetch_bytes"]),
+                   "write_bytes": round(rec["write_bytes"]), "fetch_scale": res["scales"][0],
+                   "write_scale": res["scales"][1]}
+    json.dump(tj, open(os.path.join(prof, "traffic.json"), "w"), indent=1, sort_keys=True)
+    print(res["stats"])
+    print(res["traffic_txt"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,12 +250,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama_up")
     ap.add_argument("--adapters", type=int, default=None)
-    ap.add_argument("--cpu-tokens", type=int, default=8, help="oracle sample: tokens per segment")
+    ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample: tokens per segment")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--rocprof-summary", default=None,
+                    help="directory holding rocprofv3 csv runs trace/, fetch/, write/, copy_fetch/, copy_write/: "
+                         "write summaries under profiles/ and exit")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        write_profiles(args.rocprof_summary, args.workload)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the packed-LoRA operator here has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
