@@ -58,7 +58,9 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 #pragma unroll
     for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = f32x16{};
 
-    u32x4 xq[2][4], ap[2][MAXJT][4];
+    // three register buffers of one 64-k block each: two blocks stay in flight
+    // while one is multiplied (HBM streaming needs many loads outstanding)
+    u32x4 xq[3][4], ap[3][MAXJT][4];
     auto load = [&](int buf, int64_t kb) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
             xq[buf][s] = load16_or_zero(qrow + kb + 8 * s, ok);
 #pragma unroll
             for (int jt = 0; jt < MAXJT; ++jt)
-                ap[buf][jt][s] = load16_or_zero(prow[jt] + kb + 8 * s, ok && pv[jt]);
+                ap[buf][jt][s] = load16_or_zero(prow[jt] + kb + 8 * s, ok && pv[jt] && jt < ntj);
         }
     };
     auto mma = [&](int buf) {
@@ -76,14 +78,18 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
             for (int jt = 0; jt < MAXJT; ++jt)
                 if (jt < ntj) acc[jt] = mfma32x32x16(as_bf16x8(xq[buf][s]), as_bf16x8(ap[buf][jt][s]), acc[jt]);
     };
-    // two register buffers, unrolled so each buffer index is a constant
+    // unrolled by three so every buffer index is a constant
     load(0, 0);
-    for (int64_t kb = 0; kb < K; kb += 128) {
-        if (kb + 64 < K) load(1, kb + 64);
+    if (64 < K) load(1, 64);
+    for (int64_t kb = 0; kb < K; kb += 192) {
+        if (kb + 128 < K) load(2, kb + 128);
         mma(0);
         if (kb + 64 >= K) break;
-        if (kb + 128 < K) load(0, kb + 128);
+        if (kb + 192 < K) load(0, kb + 192);
         mma(1);
+        if (kb + 128 >= K) break;
+        if (kb + 256 < K) load(1, kb + 256);
+        mma(2);
     }
 
     float* __restrict__ out = a.out + seg.hoff[i] + (t0 - s0) * r;
@@ -94,6 +100,116 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int row = 8 * (v >> 2) + 4 * lh + (v & 3);
+            if (row < nrows) out[(int64_t)row * r + j] = acc[jt][v];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined shrink (K a multiple of 64): one workgroup per 128-token tile of
+// one adapter.  Each 64-k stage brings the tile's 128 rows of X/dY and the
+// adapter's 32*MAXJT panel rows into LDS with LDS DMA (1 KiB per instruction =
+// 8 rows x 128 B, whole cache lines), three stages deep so two stay in flight;
+// wavefront w multiplies its 32 token rows against the panel.  Rows past the
+// segment, the tensor or the rank read as zero (outside the buffer range).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kShRowB = 128;                     // bytes per LDS row (64 bf16 of k)
+constexpr int kShX = kShrinkTileRows * kShRowB;  // 16 KiB of token rows per stage
+constexpr int kShStage = kShX + 128 * kShRowB;   // + up to 128 panel rows: 32 KiB
+
+__shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
+
+__device__ __forceinline__ int shofs(int r, int c) { return r * kShRowB + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+
+template <int N>
+__device__ __forceinline__ void sh_wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void sh_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MAXJT>
+__global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
+    const int tile = (int)blockIdx.x;
+    const int64_t K = a.K;
+    const int i = adapter_of_unit(m, seg.n, tile);
+    const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
+    const int64_t t0 = s0 + (int64_t)(tile - m.pre[i]) * kShrinkTileRows;
+    const int nrows = (int)(s1 - t0 < kShrinkTileRows ? s1 - t0 : kShrinkTileRows);
+    const int r = seg.rank[i];
+    const int ntj = (r + 31) >> 5;
+    const int l = lane_id(), w = wave_id(), l32 = l & 31, lh = l >> 5;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.Q) + t0 * K), 0, (int)(nrows * K * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.P) + (int64_t)seg.roff[i] * K), 0, (int)(r * K * 2), kRsrcWord3);
+    // DMA block b: rows 8b .. 8b+7; lane l -> row 8b + l/8, physical chunk l%8
+    const int r0 = l >> 3;
+    const uint32_t lane_row = (uint32_t)(r0 * K * 2);
+    const int KT = (int)(K / 64);
+    // token tile: blocks 4w .. 4w+3 (16 blocks = 128 rows); panel: blocks MAXJT*w .. (4*MAXJT blocks)
+    auto issue = [&](uint8_t* buf, int kt) {
+        const uint32_t oob = kt < KT ? 0u : 0x80000000u;
+        const uint32_t kb = (uint32_t)kt * 128u + oob;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int blk = 4 * wu + j;
+            const uint32_t vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (8u * K * 2) + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < MAXJT; ++j) {
+            const int blk = MAXJT * wu + j;
+            const uint32_t vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (8u * K * 2) + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + kShX + blk * 1024), 16, vo, 0, 0, 0);
+        }
+    };
+    f32x16 acc[MAXJT];
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = f32x16{};
+    auto compute = [&](const uint8_t* buf) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + shofs(32 * w + l32, 2 * kk + lh)));
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt) {
+                if (jt >= ntj) continue;
+                const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kShX + shofs(32 * jt + l32, 2 * kk + lh)));
+                acc[jt] = mfma32x32x16(xa, pb, acc[jt]);
+            }
+        }
+    };
+    constexpr int kPer = 4 + MAXJT;  // DMA loads per wave per stage
+    // stage kt in cur; stage kt+1 in flight in nxt; refill prv (stage kt-1, done) with stage kt+2
+    auto step = [&](uint8_t* cur, uint8_t* prv, int kt) {
+        sh_wait_vmcnt<kPer>();  // stage kt landed, stage kt+1 may be in flight
+        sh_lds_barrier();       // and every wave is done with stage kt-1
+        issue(prv, kt + 2);
+        compute(cur);
+    };
+    issue(g_sh0, 0);
+    issue(g_sh1, 1);
+    for (int kt = 0; kt < KT; kt += 3) {
+        step(g_sh0, g_sh2, kt);
+        if (kt + 1 >= KT) break;
+        step(g_sh1, g_sh0, kt + 1);
+        if (kt + 2 >= KT) break;
+        step(g_sh2, g_sh1, kt + 2);
+    }
+    sh_wait_vmcnt<0>();
+
+    // D[t][j]: lane holds rank column j, token rows 8*(v/4) + 4*(l/32) + v%4 of its wave's 32
+    float* __restrict__ out = a.out + seg.hoff[i] + (t0 - s0) * r;
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) {
+        const int j = jt * 32 + l32;
+        if (jt >= ntj || j >= r) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = 32 * w + 8 * (v >> 2) + 4 * lh + (v & 3);
             if (row < nrows) out[(int64_t)row * r + j] = acc[jt][v];
         }
     }
@@ -270,6 +386,19 @@ __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, W
 hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st) {
     if (units <= 0) return hipSuccess;
+    if (a.K % 64 == 0 && (int64_t)kShrinkTileRows * a.K * 2 < (int64_t(1) << 31) &&
+        (int64_t)s.roff[s.n] * a.K * 2 < (int64_t(1) << 31)) {
+        WorkMap m128;
+        const int32_t tiles = build_shrink_map(s, &m128, kShrinkTileRows);
+        const dim3 grid((unsigned)tiles), block(256);
+        switch ((s.rmax + 31) / 32) {
+            case 1: hipLaunchKernelGGL(shrink_bf16_pipe<1>, grid, block, 0, st, a, s, m128); break;
+            case 2: hipLaunchKernelGGL(shrink_bf16_pipe<2>, grid, block, 0, st, a, s, m128); break;
+            case 3: hipLaunchKernelGGL(shrink_bf16_pipe<3>, grid, block, 0, st, a, s, m128); break;
+            default: hipLaunchKernelGGL(shrink_bf16_pipe<4>, grid, block, 0, st, a, s, m128); break;
+        }
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
     const int jt = (s.rmax + 31) / 32;
     switch (jt) {

@@ -69,12 +69,12 @@ void build_segtable(const plora_desc* d, SegTable* s) {
     s->rmax = rmax;
 }
 
-int32_t build_shrink_map(const SegTable& s, WorkMap* m) {
+int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows) {
     int32_t t = 0;
     for (int i = 0; i < s.n; ++i) {
         m->pre[i] = t;
         const int64_t ni = s.off[i + 1] - s.off[i];
-        t += (int32_t)((ni + kShrinkRows - 1) / kShrinkRows);
+        t += (int32_t)((ni + rows - 1) / rows);
     }
     m->pre[s.n] = t;
     return t;

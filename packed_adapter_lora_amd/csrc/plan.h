@@ -19,8 +19,10 @@ namespace plora {
 constexpr int kMaxN = PLORA_MAX_ADAPTERS;
 constexpr int kMaxRank = PLORA_MAX_RANK;
 
-// Token rows per shrink work unit (one wavefront computes a 32-row tile).
+// Token rows per shrink work unit: 32 (one wavefront) in the general kernel,
+// 128 (one workgroup of four wavefronts) in the pipelined one.
 constexpr int kShrinkRows = 32;
+constexpr int kShrinkTileRows = 128;
 
 // Per-adapter table, passed to kernels by value (about 1.8 KiB of kernel
 // arguments; N <= 64 keeps it well under the 4 KiB argument limit, so no
@@ -56,8 +58,8 @@ int validate_desc(const plora_desc* d, const char** why);
 // Fills the segment table of a validated descriptor.
 void build_segtable(const plora_desc* d, SegTable* s);
 
-// Shrink tiles: ceil(n_i / kShrinkRows) per adapter.  Returns the total.
-int32_t build_shrink_map(const SegTable& s, WorkMap* m);
+// Shrink tiles: ceil(n_i / rows) per adapter.  Returns the total.
+int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows = kShrinkRows);
 
 // Token-chunk size of the weight-gradient reduction over a feature width D.
 // It depends only on D, so an adapter's reduction order is the same whether
