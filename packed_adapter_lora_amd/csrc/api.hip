@@ -226,15 +226,19 @@ int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, cons
         WgradPlan pa, pb;
         build_wgrad_plan(s, d->d_in, &pa);
         build_wgrad_plan(s, d->d_out, &pb);
-        float* part_a = static_cast<float*>(ws);
-        float* part_b = part_a ? part_a + (((size_t)pa.part_elems * 4 + 255) & ~(size_t)255) / 4 : nullptr;
+        const WorkspaceLayout wl = workspace_layout(s, d->d_in, d->d_out);
+        uint8_t* wsb = static_cast<uint8_t*>(ws);
+        float* part_a = wsb ? reinterpret_cast<float*>(wsb + wl.part_a) : nullptr;
+        float* part_b = wsb ? reinterpret_cast<float*>(wsb + wl.part_b) : nullptr;
+        __bf16* g_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_g) : nullptr;
+        __bf16* h_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_h) : nullptr;
         const WgradArgs wb{dY, H, dB, part_b, d->d_out};
         const WgradArgs wa{X, G, dA, part_a, d->d_in};
-        e = timed("wgrad", st, [&] { return launch_wgrad_bf16(wb, s, pb, st); });
+        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st); });
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
         e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
         if (e != hipSuccess) return hip_fail(e, "reduce launch");
-        e = timed("wgrad", st, [&] { return launch_wgrad_bf16(wa, s, pa, st); });
+        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st); });
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
         e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
         if (e != hipSuccess) return hip_fail(e, "reduce launch");

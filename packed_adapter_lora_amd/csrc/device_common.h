@@ -62,4 +62,46 @@ __device__ __forceinline__ int adapter_of_unit(const WorkMap& m, int n, int32_t 
     return i;
 }
 
+// ---- LDS DMA pipelines (shared by the GEMM, shrink and weight-gradient kernels)
+
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+
+// Byte offset of 16-byte chunk c of row r in a tile of 128-byte rows.  The XOR
+// keeps any 16 (or 8) consecutive rows read at one chunk on distinct banks.
+__device__ __forceinline__ int kofs128(int r, int c) { return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
+
+// Byte offset of 16-byte chunk c of row k in a tile of 512-byte rows read
+// transposed: chunk c of row k is stored at c ^ 4*(k%4), so the 16 lanes of a
+// transposed read (4 rows x 32 bytes) and the next 16 hit distinct banks.
+__device__ __forceinline__ int tofs(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
+
+typedef __bf16 bf16x4v __attribute__((vector_size(8)));
+
+// 8 consecutive rows k of column p from a tile of 512-byte rows, as one MFMA
+// operand, with two transposed LDS reads (ds_read_b64_tr_b16).  Within each
+// 16-lane group, lane L supplies the address of row kb + L/4, columns
+// pc + 4*(L%4) .. +3, and lane i gets back rows kb..kb+3 of column pc + i.
+// Lane l receives column p0 + l%32, rows kb + 8*(l/32) .. +7.
+__device__ __forceinline__ bf16x8 pfrag_tr(const uint8_t* tile, int p0, int kb) {
+    const int l = lane_id(), L = l & 15, g = l >> 4;
+    const int p = p0 + 16 * (g & 1) + 4 * (L & 3);
+    const int k = kb + 8 * (g >> 1) + (L >> 2);
+    const uint8_t* a0 = tile + tofs(k, p >> 3) + (p & 7) * 2;
+    const uint8_t* a1 = tile + tofs(k + 4, p >> 3) + (p & 7) * 2;
+    typedef __attribute__((address_space(3))) bf16x4v lds_v4;
+    const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a0));
+    const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// workgroup barrier for LDS only: wait for this wave's LDS reads, then s_barrier
+// (no vmcnt drain, so in-flight prefetches stay in flight)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace plora

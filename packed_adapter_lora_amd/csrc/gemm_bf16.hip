@@ -337,10 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTab
 // barrier per stage, before the last step, after which the freed buffer is
 // refilled with stage k+2 while the last step runs.
 // ===========================================================================
-typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kPipeTile = 256 * kKRow;           // 32 KiB: 256 rows x 128 B
 constexpr int kPipeStage = 2 * kPipeTile;        // 64 KiB
-constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data format (gfx9 family)
 #ifndef PLORA_DMA_SPLIT
 #define PLORA_DMA_SPLIT 8                         // of a stage's 16 loads per wave, issued one step later
 #endif
@@ -348,37 +346,6 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data form
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kPipeStage];
 __shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kPipeStage];
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-// workgroup barrier for LDS only: wait for this wave's LDS reads, then s_barrier
-// (no vmcnt drain, so in-flight prefetches stay in flight)
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// p-contiguous weight tile (backward): 64 k-rows x 512 B; the 16-byte chunk c of
-// row k is stored at chunk c ^ 4*(k%4), so the 16 lanes of a transposed read
-// (4 rows x 32 bytes) and the next 16 (the next 32 bytes) hit distinct banks.
-__device__ __forceinline__ int tofs(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
-
-typedef __bf16 bf16x4v __attribute__((vector_size(8)));
-
-// 8 consecutive k of feature p from a p-contiguous tile with two transposed
-// LDS reads (ds_read_b64_tr_b16).  Within each 16-lane group, lane L supplies
-// the address of k-row kb + L/4, features pc + 4*(L%4) .. +3, and lane i gets
-// back rows kb..kb+3 of feature pc + i.
-__device__ __forceinline__ bf16x8 pfrag_tr(const uint8_t* tile, int prow0, int kb) {
-    const int l = lane_id(), L = l & 15, g = l >> 4;
-    const int p = prow0 + 16 * (g & 1) + 4 * (L & 3);
-    const int k = kb + 8 * (g >> 1) + (L >> 2);
-    const uint8_t* a0 = tile + tofs(k, p >> 3) + (p & 7) * 2;
-    const uint8_t* a1 = tile + tofs(k + 4, p >> 3) + (p & 7) * 2;
-    typedef __attribute__((address_space(3))) bf16x4v lds_v4;
-    const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a0));
-    const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));
-    bf16x8 r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-    return r;
-}
 
 template <bool P_KMAJOR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, SegTable seg) {
@@ -450,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
             if constexpr (P_KMAJOR)
                 fa[s][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kmaj(wp * 128 + m * 32 + l32, 2 * kk + lh)));
             else
-                fa[s][m] = pfrag_tr(buf, wp * 128 + m * 32, 16 * kk);
+                fa[s][m] = pfrag_tr(buf, wp * 128 + m * 32, 16 * kk);  // p-contiguous weight tile
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n)

@@ -46,6 +46,10 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
 hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st);
 hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);
+// Pipelined weight gradient: first writes the transposed hi/lo bf16 copy of F
+// (plan.ft_elems elements each) into fhi / flo, then reduces over tokens.
+hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, __bf16* fhi, __bf16* flo,
+                                  hipStream_t st);
 hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);
 
 hipError_t launch_gemm_f32(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);

@@ -113,8 +113,6 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 // wavefront w multiplies its 32 token rows against the panel.  Rows past the
 // segment, the tensor or the rank read as zero (outside the buffer range).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kShRowB = 128;                     // bytes per LDS row (64 bf16 of k)
 constexpr int kShX = kShrinkTileRows * kShRowB;  // 16 KiB of token rows per stage
 constexpr int kShStage = kShX + 128 * kShRowB;   // + up to 128 panel rows: 32 KiB
@@ -123,11 +121,6 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
 
-__device__ __forceinline__ int shofs(int r, int c) { return r * kShRowB + ((c ^ ((r ^ (r >> 3)) & 7)) << 4); }
-
-template <int N>
-__device__ __forceinline__ void sh_wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-__device__ __forceinline__ void sh_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int MAXJT>
 __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
@@ -173,11 +166,11 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
     auto compute = [&](const uint8_t* buf) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + shofs(32 * w + l32, 2 * kk + lh)));
+            const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kofs128(32 * w + l32, 2 * kk + lh)));
 #pragma unroll
             for (int jt = 0; jt < MAXJT; ++jt) {
                 if (jt >= ntj) continue;
-                const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kShX + shofs(32 * jt + l32, 2 * kk + lh)));
+                const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kShX + kofs128(32 * jt + l32, 2 * kk + lh)));
                 acc[jt] = mfma32x32x16(xa, pb, acc[jt]);
             }
         }
@@ -185,8 +178,8 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
     constexpr int kPer = 4 + MAXJT;  // DMA loads per wave per stage
     // stage kt in cur; stage kt+1 in flight in nxt; refill prv (stage kt-1, done) with stage kt+2
     auto step = [&](uint8_t* cur, uint8_t* prv, int kt) {
-        sh_wait_vmcnt<kPer>();  // stage kt landed, stage kt+1 may be in flight
-        sh_lds_barrier();       // and every wave is done with stage kt-1
+        wait_vmcnt<kPer>();  // stage kt landed, stage kt+1 may be in flight
+        lds_barrier();       // and every wave is done with stage kt-1
         issue(prv, kt + 2);
         compute(cur);
     };
@@ -199,7 +192,7 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
         if (kt + 2 >= KT) break;
         step(g_sh2, g_sh1, kt + 2);
     }
-    sh_wait_vmcnt<0>();
+    wait_vmcnt<0>();
 
     // D[t][j]: lane holds rank column j, token rows 8*(v/4) + 4*(l/32) + v%4 of its wave's 32
     float* __restrict__ out = a.out + seg.hoff[i] + (t0 - s0) * r;
@@ -364,6 +357,162 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined weight gradient.
+//
+// wgrad_prep writes the fp32 H_i (or G_i) block [n_i][r_i] transposed as two
+// bf16 arrays hi = bf16(v), lo = bf16(v - hi), row j of length pad64(n_i)
+// (zero-padded), so the main kernel can stream it as whole 128-byte lines.
+//
+// wgrad_bf16_pipe: one workgroup per (adapter token chunk, 256 features).
+// Each 64-token stage brings the chunk's X/dY rows (64 x 512 B, read
+// transposed: MFMA B = features, K = tokens) and the adapter's hi/lo rank
+// panels (32*MAXJT rows x 128 B each, MFMA A = rank rows) into LDS with LDS
+// DMA; three stages, two in flight (ranks up to 64; larger ranks use the
+// register-staged kernel above).  Tokens past the chunk read as zero
+// (outside the buffer range or zero padding).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void wgrad_prep(const float* F, bf16* hi, bf16* lo, SegTable seg, WgradPlan plan) {
+    const int g = (int)blockIdx.y;  // global rank row R_off[i] + j
+    int i = 0;
+    while (i + 1 < seg.n && seg.roff[i + 1] <= g) ++i;
+    const int j = g - seg.roff[i];
+    const int r = seg.rank[i];
+    const int64_t n = seg.off[i + 1] - seg.off[i];
+    const int64_t np = pad64(n);
+    const float* __restrict__ Fi = F + seg.hoff[i];
+    bf16* __restrict__ h = hi + plan.ft_off[i] + (int64_t)j * np;
+    bf16* __restrict__ o = lo + plan.ft_off[i] + (int64_t)j * np;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < np; u += (int64_t)gridDim.x * 256) {
+        const float v = u < n ? Fi[u * r + j] : 0.0f;
+        bf16 hb, lb;
+        split_bf16(v, hb, lb);
+        h[u] = hb;
+        o[u] = lb;
+    }
+}
+
+constexpr int kWqTile = 64 * 512;  // 64 tokens x 256 features bf16
+
+template <int MAXJT>
+__global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable seg, WgradPlan plan, const bf16* fhi,
+                                                          const bf16* flo) {
+    constexpr int kF = 32 * MAXJT * 128;       // one of the hi / lo panels
+    constexpr int kStage = kWqTile + 2 * kF;
+    __shared__ __attribute__((aligned(1024))) uint8_t b0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t b1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t b2[kStage];
+    const int64_t D = a.D;
+    const int w = (int)blockIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.y * kWgCols;
+    const int i = adapter_of_unit(plan.chunks, seg.n, w);
+    const int u = w - plan.chunks.pre[i];
+    const int nchunks = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
+    const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
+    const int TK = plan.chunk_tokens;
+    const int64_t ta = s0 + (int64_t)u * TK;
+    const int64_t tb = ta + TK < s1 ? ta + TK : s1;
+    const int64_t np = pad64(s1 - s0);
+    const int r = seg.rank[i];
+    const int ntj = (r + 31) >> 5;
+    const int l = lane_id(), wv = wave_id(), l32 = l & 31, lh = l >> 5;
+    const int wu = __builtin_amdgcn_readfirstlane(wv);
+
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.Q) + ta * D + c0), 0, (int)(((tb - ta - 1) * D + (D - c0)) * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(fhi + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(flo + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
+    // activation tile: block b = 2 token rows x 512 B; lane l -> row 2b + l/32, physical chunk l%32
+    // (row % 4 = 2*(b%2) + l/32: one lane offset per block parity)
+    const int tr = l >> 5;
+    const uint32_t q_off0 = (uint32_t)(tr * D * 2) + (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
+    const uint32_t q_off1 = (uint32_t)(tr * D * 2) + (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
+    // rank panels: block b = 8 rank rows x 128 B; lane l -> row 8b + l/8, physical chunk l%8
+    const int r0 = l >> 3;
+    const uint32_t f_row = (uint32_t)(r0 * np * 2);
+    const int nst = (int)((tb - ta + 63) / 64);
+    auto issue = [&](uint8_t* buf, int st) {
+        const uint32_t oob = st < nst ? 0u : 0x80000000u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int blk = 8 * wu + j;
+            const uint32_t vo = ((j & 1) ? q_off1 : q_off0) + (uint32_t)blk * (uint32_t)(2 * D * 2) +
+                                (uint32_t)st * (uint32_t)(64 * D * 2) + oob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < MAXJT; ++j) {
+            const int blk = MAXJT * wu + j;
+            const uint32_t vo = f_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (uint32_t)(8 * np * 2) +
+                                (uint32_t)st * 128u + oob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)(buf + kWqTile + blk * 1024), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(buf + kWqTile + kF + blk * 1024), 16, vo, 0, 0, 0);
+        }
+    };
+    f32x16 acc[MAXJT][2];
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) acc[jt][0] = acc[jt][1] = f32x16{};
+    auto compute = [&](const uint8_t* buf) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 qf[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) qf[ct] = pfrag_tr(buf, 64 * wv + 32 * ct, 16 * kk);
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt) {
+                if (jt >= ntj) continue;
+                const int row = 32 * jt + l32;
+                const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kWqTile + kofs128(row, 2 * kk + lh)));
+                const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kWqTile + kF + kofs128(row, 2 * kk + lh)));
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    acc[jt][ct] = mfma32x32x16(ah, qf[ct], acc[jt][ct]);
+                    acc[jt][ct] = mfma32x32x16(al, qf[ct], acc[jt][ct]);
+                }
+            }
+        }
+    };
+    constexpr int kPer = 8 + 2 * MAXJT;  // DMA loads per wave per stage
+    auto step = [&](uint8_t* cur, uint8_t* prv, int st) {
+        wait_vmcnt<kPer>();  // stage st landed, st+1 may be in flight
+        lds_barrier();       // every wave is done with stage st-1
+        issue(prv, st + 2);
+        compute(cur);
+    };
+    issue(b0, 0);
+    issue(b1, 1);
+    for (int st = 0; st < nst; st += 3) {
+        step(b0, b2, st);
+        if (st + 1 >= nst) break;
+        step(b1, b0, st + 1);
+        if (st + 2 >= nst) break;
+        step(b2, b1, st + 2);
+    }
+    wait_vmcnt<0>();
+
+    // D[j][c]: lane holds feature column c, rank rows 8*(v/4) + 4*(l/32) + v%4.
+    const bool direct = nchunks == 1;
+    const float sc = seg.scale[i];
+    float* __restrict__ dst = direct ? a.out + (int64_t)seg.roff[i] * D
+                                     : a.part + plan.part_off[i] + (int64_t)u * r * D;
+#pragma unroll
+    for (int jt = 0; jt < MAXJT; ++jt) {
+        if (jt >= ntj) continue;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int64_t c = c0 + wv * 64 + ct * 32 + l32;
+            if (c >= D) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if (j < r) dst[(int64_t)j * D + c] = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+            }
+        }
+    }
+}
+
 // out rows of adapters whose tokens span 0 or >= 2 chunks:
 // out = s_i * sum_u partial[u] in chunk order (0 for an empty adapter).
 __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, WgradPlan plan) {
@@ -421,6 +570,31 @@ hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradP
         case 3: hipLaunchKernelGGL(wgrad_bf16<3>, grid, block, 0, st, a, s, p); break;
         default: hipLaunchKernelGGL(wgrad_bf16<4>, grid, block, 0, st, a, s, p); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, bf16* fhi, bf16* flo,
+                                  hipStream_t st) {
+    const int64_t tk = p.chunk_tokens;
+    if (s.rmax > 64 || fhi == nullptr || tk * a.D * 2 >= (int64_t(1) << 31)) return launch_wgrad_bf16(a, s, p, st);
+    const int R = s.roff[s.n];
+    if (R > 0) {
+        int64_t maxnp = 0;
+        for (int i = 0; i < s.n; ++i) maxnp = maxnp > pad64(s.off[i + 1] - s.off[i]) ? maxnp : pad64(s.off[i + 1] - s.off[i]);
+        if (maxnp > 0) {
+            const int64_t bx = (maxnp + 255) / 256 < 64 ? (maxnp + 255) / 256 : 64;
+            hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)bx, (unsigned)R), dim3(256), 0, st, a.F, fhi, flo, s, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    const int32_t units = p.chunks.pre[s.n];
+    if (units <= 0) return hipSuccess;
+    const dim3 grid((unsigned)units, (unsigned)p.col_tiles), block(256);
+    if (s.rmax <= 32)
+        hipLaunchKernelGGL((wgrad_bf16_pipe<1>), grid, block, 0, st, a, s, p, fhi, flo);
+    else
+        hipLaunchKernelGGL((wgrad_bf16_pipe<2>), grid, block, 0, st, a, s, p, fhi, flo);
     return hipGetLastError();
 }
 

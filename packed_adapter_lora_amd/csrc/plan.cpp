@@ -87,27 +87,41 @@ void build_wgrad_plan(const SegTable& s, int64_t D, WgradPlan* p) {
     p->chunk_tokens = wgrad_chunk_tokens(D);
     p->col_tiles = (int32_t)((D + 255) / 256);
     int32_t c = 0;
-    int64_t po = 0;
+    int64_t po = 0, fo = 0;
     for (int i = 0; i < s.n; ++i) {
         const int64_t ni = s.off[i + 1] - s.off[i];
         const int32_t ci = (int32_t)((ni + p->chunk_tokens - 1) / p->chunk_tokens);
         p->chunks.pre[i] = c;
         p->part_off[i] = po;
+        p->ft_off[i] = fo;
         c += ci;
         if (ci > 1) po += (int64_t)ci * s.rank[i] * D;
+        fo += (int64_t)s.rank[i] * pad64(ni);
     }
     p->chunks.pre[s.n] = c;
     p->part_off[s.n] = po;
     p->part_elems = po;
+    p->ft_off[s.n] = fo;
+    p->ft_elems = fo;
 }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out) {
+WorkspaceLayout workspace_layout(const SegTable& s, int64_t d_in, int64_t d_out) {
     WgradPlan a, b;
     build_wgrad_plan(s, d_in, &a);
     build_wgrad_plan(s, d_out, &b);
-    return round256((size_t)a.part_elems * 4) + round256((size_t)b.part_elems * 4);
+    WorkspaceLayout w;
+    w.part_a = 0;
+    w.part_b = w.part_a + round256((size_t)a.part_elems * 4);
+    w.ft_g = w.part_b + round256((size_t)b.part_elems * 4);
+    w.ft_h = w.ft_g + round256((size_t)a.ft_elems * 2 * 2);
+    w.total = w.ft_h + round256((size_t)b.ft_elems * 2 * 2);
+    return w;
+}
+
+size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out) {
+    return workspace_layout(s, d_in, d_out).total;
 }
 
 }  // namespace plora

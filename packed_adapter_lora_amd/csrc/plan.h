@@ -50,7 +50,13 @@ struct WgradPlan {
     WorkMap chunks;            // token chunks per adapter
     int64_t part_off[kMaxN + 1];  // fp32 element offset of adapter i's partials
     int64_t part_elems;        // total partial elements
+    int64_t ft_off[kMaxN + 1];    // bf16 element offset of adapter i's transposed H/G block
+    int64_t ft_elems;          // sum_i r_i * pad64(n_i): one of the hi / lo arrays
 };
+
+// Tokens of adapter i rounded up to a multiple of 64 (rows of the transposed
+// bf16 H/G blocks the weight-gradient kernel streams).
+constexpr int64_t pad64(int64_t n) { return (n + 63) & ~int64_t(63); }
 
 // Returns a plora_status; checks only the descriptor (no pointers to data).
 int validate_desc(const plora_desc* d, const char** why);
@@ -71,8 +77,12 @@ int32_t wgrad_chunk_tokens(int64_t D);
 // elements); the rest are written directly.
 void build_wgrad_plan(const SegTable& s, int64_t D, WgradPlan* p);
 
-// Workspace bytes of plora_backward_dAdB: partials of dA and dB, each rounded
-// up to 256 bytes.
+// Workspace of plora_backward_dAdB, each region rounded up to 256 bytes:
+// [dA partials fp32][dB partials fp32][G^T hi, lo bf16][H^T hi, lo bf16].
+struct WorkspaceLayout {
+    size_t part_a, part_b, ft_g, ft_h, total;  // byte offsets and total
+};
+WorkspaceLayout workspace_layout(const SegTable& s, int64_t d_in, int64_t d_out);
 size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out);
 
 }  // namespace plora

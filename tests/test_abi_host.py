@@ -77,13 +77,18 @@ def test_validation_codes(P):
 def test_sizes(P):
     d = desc(P, counts=(3, 0, 5), ranks=(4, 8, 16))
     assert P.plora_h_elems(d) == 3 * 4 + 0 + 5 * 16
-    # small adapters fit one token chunk: no partials
-    assert P.plora_workspace_bytes(d) == 0
+    # workspace = [dA partials][dB partials][G^T hi+lo][H^T hi+lo], each rounded to 256 B;
+    # the transposed blocks hold r_i rows of pad64(n_i) bf16 tokens
+    r256 = lambda b: (b + 255) // 256 * 256
+    pad64 = lambda n: (n + 63) // 64 * 64
+    ft = r256((4 * pad64(3) + 8 * pad64(0) + 16 * pad64(5)) * 2 * 2)
+    assert P.plora_workspace_bytes(d) == 0 + 0 + 2 * ft
     big = desc(P, counts=(5000, 1, 0), ranks=(64, 8, 16), d_in=4096, d_out=16384)
     # d_in <= 8192: 1024-token chunks; d_out > 8192: 2048-token chunks; only adapter 0 is split
     a = 5 * 64 * 4096 * 4
     b = 3 * 64 * 16384 * 4
-    assert P.plora_workspace_bytes(big) == ((a + 255) // 256) * 256 + ((b + 255) // 256) * 256
+    ft = r256((64 * pad64(5000) + 8 * pad64(1) + 16 * pad64(0)) * 2 * 2)
+    assert P.plora_workspace_bytes(big) == r256(a) + r256(b) + 2 * ft
     assert P.plora_workspace_bytes(desc(P, d_in=12)) == 0  # invalid -> 0
     assert P.plora_workspace_bytes(desc(P, dtype="f32")) == 0
 
