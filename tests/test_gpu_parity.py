@@ -63,6 +63,25 @@ def test_bf16_multitile_full(P):
     full_case(P, wl)
 
 
+def test_bf16_pipelined_tails_full(P):
+    # pipelined GEMMs (K % 128 == 0 both ways) with a feature tail in both
+    # orientations (640 % 256, 384 % 256) and a token tail (777 % 256)
+    wl = workloads.custom(384, 640, [100, 0, 513, 1, 163], [16, 8, 64, 32, 1], [32.0, 16.0, 8.0, 16.0, 4.0],
+                          "bf16", seed=29, name="pipe_tails_bf16")
+    full_case(P, wl)
+
+
+def test_max_adapters_and_rank(P):
+    # 64 adapters (the ABI maximum), ranks up to 128 (the maximum), empty and 1-token segments
+    n = 64
+    counts = [(i * 37) % 97 if i % 9 else 0 for i in range(n)]
+    counts[5] = 1
+    ranks = [128 if i % 16 == 0 else (i % 8) * 8 + 1 for i in range(n)]
+    alphas = [float(2 * r) for r in ranks]
+    wl = workloads.custom(256, 512, counts, ranks, alphas, "bf16", seed=30, name="max_adapters")
+    full_case(P, wl)
+
+
 def test_f32_ragged_full(P):
     wl = workloads.custom(136, 72, [5, 0, 33, 70], [3, 7, 16, 64], [6.0, 7.0, 32.0, 16.0], "f32", seed=23,
                           name="ragged_f32")
@@ -134,11 +153,16 @@ def test_rank1_indexing_exact(P, dtype):
         assert np.array_equal(gpu[k], ref[k]), k
 
 
-def test_b_zero_matches_frozen_path_bitwise(P):
+# (d_in, d_out): general kernels (K not a multiple of 128) and pipelined kernels
+SHAPES = [(320, 264), (512, 768)]
+
+
+@pytest.mark.parametrize("d_in,d_out", SHAPES)
+def test_b_zero_matches_frozen_path_bitwise(P, d_in, d_out):
     """B = 0 (LoRA's initial state): Y and dX equal the N = 0 results bit for bit,
     G and dA are exactly zero."""
     import torch
-    wl = workloads.custom(320, 264, [100, 0, 300, 7], [8, 16, 64, 128], [16.0, 32.0, 8.0, 256.0], "bf16",
+    wl = workloads.custom(d_in, d_out, [100, 0, 300, 7], [8, 16, 64, 128], [16.0, 32.0, 8.0, 256.0], "bf16",
                           seed=26, name="bzero")
     log("case %s" % wl.name)
     inp = workloads.make_inputs(wl)
@@ -171,10 +195,11 @@ def test_reproducible_bitwise(P):
                            b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k].view(torch.int32)), k
 
 
-def test_packed_equals_separate_bitwise(P):
+@pytest.mark.parametrize("d_in,d_out", [(320, 1032), (512, 768)])
+def test_packed_equals_separate_bitwise(P, d_in, d_out):
     """The packed call gives each adapter exactly what a call with that adapter alone gives."""
     import torch
-    wl = workloads.custom(320, 1032, [129, 0, 2200, 31, 600], [16, 8, 64, 1, 33], [32.0, 16.0, 8.0, 2.0, 66.0],
+    wl = workloads.custom(d_in, d_out, [129, 0, 2200, 31, 600], [16, 8, 64, 1, 33], [32.0, 16.0, 8.0, 2.0, 66.0],
                           "bf16", seed=28, name="packed_vs_separate")
     log("case %s" % wl.name)
     inp = workloads.make_inputs(wl)
