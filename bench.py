@@ -195,6 +195,53 @@ def run_bench(wl, steps, warmup):
     return (t1 - t0) / steps, kern, inp
 
 
+def run_loop_bench(wl, steps, warmup):
+    """The same tokens computed adapter by adapter: one single-adapter call per
+    segment for each of forward, backward_dx and backward_dAdB (the sequential
+    execution that packing replaces).  Returns seconds per step."""
+    import torch
+    import packed_adapter_lora_amd as P
+    _, dev = make_device_inputs(wl)
+    dt = dev["X"].dtype
+    Y = torch.empty((wl.T, wl.d_out), dtype=dt, device="cuda")
+    dX = torch.empty((wl.T, wl.d_in), dtype=dt, device="cuda")
+    he = int(np.sum(np.diff(wl.offsets) * wl.ranks))
+    H = torch.empty((he,), dtype=torch.float32, device="cuda")
+    G = torch.empty((he,), dtype=torch.float32, device="cuda")
+    dA = torch.empty((wl.R, wl.d_in), dtype=torch.float32, device="cuda")
+    dB = torch.empty((wl.R, wl.d_out), dtype=torch.float32, device="cuda")
+    calls = []
+    ro = ho = 0
+    for i in range(wl.n_adapters):
+        a, b = int(wl.offsets[i]), int(wl.offsets[i + 1])
+        r = int(wl.ranks[i])
+        d = P.Desc([0, b - a], [r], [float(wl.alphas[i])], wl.d_in, wl.d_out, wl.dtype)
+        nb = P.plora_workspace_bytes(d)
+        ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
+        calls.append((d, slice(a, b), slice(ro, ro + r), slice(ho, ho + (b - a) * r), ws))
+        ro += r
+        ho += (b - a) * r
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for d, rows, rr, hs, ws in calls:
+            P.plora_forward(d, dev["X"][rows], dev["W"], dev["A"][rr], dev["B"][rr], Y[rows], H[hs], stream)
+            P.plora_backward_dx(d, dev["dY"][rows], dev["W"], dev["A"][rr], dev["B"][rr], dX[rows], G[hs], stream)
+            P.plora_backward_dAdB(d, dev["X"][rows], dev["dY"][rows], H[hs], G[hs], dA[rr], dB[rr], ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del Y, dX, H, G, dA, dB, dev
+    torch.cuda.empty_cache()
+    return (t1 - t0) / steps
+
+
 def cpu_baseline(wl, inp, per_segment):
     """fp64 oracle on the first `per_segment` tokens of every segment: Y, H, dX,
     G and dA/dB over those tokens, as the oracle stands."""
@@ -327,8 +374,11 @@ def main():
         for n in (2, 4, 8, 16, 32):
             w2 = workloads.config(args.workload, n_adapters=n)
             s2, k2, _ = run_bench(w2, args.steps, args.warmup)
+            s3 = run_loop_bench(w2, max(3, args.steps // 4), 2)
             print(json.dumps({"sweep": True, "workload": w2.name, "n_adapters": n, "tokens": w2.T,
                               "tokens_per_s": round(w2.T / s2, 1), "ms_per_step": round(s2 * 1e3, 4),
+                              "adapter_by_adapter_tokens_per_s": round(w2.T / s3, 1),
+                              "packing_gain": round(s3 / s2, 3),
                               "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in k2.items()}}),
                   flush=True)
 

@@ -42,7 +42,7 @@ constexpr int kPRow = kBP * 2 + 16;            // bytes per p-contiguous row (pa
 constexpr int kPTile = kBK * kPRow;            // 33792 B
 constexpr int kStage = kPTile + kKTile;        // P tile (either layout) + Q tile
 constexpr int kLds = 2 * kStage;               // 132 KiB
-constexpr int kGroupQ = 8;                     // token tiles per L2 group
+constexpr int kGroupQ = 2;                     // token tiles per L2 group
 
 // Byte offset of 16-byte chunk c of row r in a K-contiguous tile.  The XOR
 // keeps the 16 rows read by any 16 lanes (and any 8) on distinct bank groups.
@@ -50,8 +50,10 @@ __device__ __forceinline__ int kmaj(int r, int c) { return r * kKRow + ((c ^ ((r
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
 // renumber so each XCD gets a contiguous range of tiles, and walk that range
-// in groups of kGroupQ token tiles so concurrent workgroups on one XCD share
-// X/dY and W panels in that XCD's L2.
+// in groups of kGroupQ token tiles: the ~32 workgroups an XCD runs at once then
+// cover 2 token tiles x 16 feature tiles, so the two X/dY panels (2 x 2 MiB at
+// K = 4096) stay in that XCD's 4 MB L2 and the weight panels, re-read more
+// often, come from the 256 MB Infinity Cache (measured best of 1, 2, 4, 8).
 __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_q, int tiles_p, int& tq, int& tp) {
     const int base = nwg / 8, extra = nwg % 8;
     const int xcd = bid % 8, slot = bid / 8;
