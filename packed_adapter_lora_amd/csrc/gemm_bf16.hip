@@ -326,27 +326,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTab
 
 
 // ===========================================================================
-// Pipelined forward kernel (K-contiguous weight, K a multiple of 128).
+// Pipelined kernel (K a multiple of 128).
 //
 // Global -> LDS without registers: buffer_load_dwordx4 ... lds (gfx950 LDS
-// DMA, 16 bytes per lane, 1 KiB per instruction = 8 rows x 128 bytes, i.e.
-// whole cache lines).  Two LDS stages of BK = 64 (64 KiB each: weight tile
-// then token tile, 128-byte rows, XOR-swizzled 16-byte chunks); each stage
-// buffer is its own __shared__ array so the compiler can tell which LDS DMA a
-// fragment read depends on.  Rows past the tensor's end fall outside the
-// buffer resource's range and read as zero.  Per stage: four k16 steps of 16
-// MFMAs per wave; the fragments of step s+1 are read while step s runs; one
-// barrier per stage, before the last step, after which the freed buffer is
-// refilled with stage k+2 while the last step runs.
+// DMA, 16 bytes per lane, 1 KiB per instruction = 8 rows x 128 bytes or 2
+// rows x 512 bytes, i.e. whole cache lines).  Tiles are BK = 64 deep, 32 KiB
+// each.  The token tile is triple-buffered and loaded two stages ahead: it is
+// shared by the 16 or so feature tiles an XCD runs at once, so every one of
+// them waits on the same L2 miss, and that wait is the one worth hiding.  The
+// weight tile is double-buffered and loaded one stage ahead.  5 x 32 KiB = all
+// 160 KiB of LDS.  Each buffer is its own __shared__ array so the compiler can
+// tell which LDS DMA a fragment read depends on; the 6-stage rotation is
+// unrolled so every buffer choice is static.  Rows past the tensor's end fall
+// outside the buffer resource's range and read as zero.  Per stage: four k16
+// steps of 16 MFMAs per wave; the fragments of step s+1 are read while step s
+// runs; one barrier per stage, before the last step.
 // ===========================================================================
-constexpr int kPipeTile = 256 * kKRow;           // 32 KiB: 256 rows x 128 B
-constexpr int kPipeStage = 2 * kPipeTile;        // 64 KiB
-#ifndef PLORA_DMA_SPLIT
-#define PLORA_DMA_SPLIT 8                         // of a stage's 16 loads per wave, issued one step later
-#endif
+constexpr int kPipeTile = 256 * kKRow;           // 32 KiB: 256 rows x 128 B (or 64 rows x 512 B)
 
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage0[kPipeStage];
-__shared__ __attribute__((aligned(1024))) uint8_t g_stage1[kPipeStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_t0[kPipeTile];  // token tiles (3)
+__shared__ __attribute__((aligned(1024))) uint8_t g_t1[kPipeTile];
+__shared__ __attribute__((aligned(1024))) uint8_t g_t2[kPipeTile];
+__shared__ __attribute__((aligned(1024))) uint8_t g_w0[kPipeTile];  // weight tiles (2)
+__shared__ __attribute__((aligned(1024))) uint8_t g_w1[kPipeTile];
 
 
 template <bool P_KMAJOR>
@@ -386,24 +388,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     const uint32_t blk_stride_t = (uint32_t)(2 * Pdim * 2);  // 2 k-rows
     const int KT = (int)(K / 64);
     const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: LDS DMA bases stay scalar
-    // loads j0 .. j1-1 of this wave's 16 for stage kt (0..7: weight tile, 8..15: token tile)
-    auto issue = [&](uint8_t* buf, int kt, int j0, int j1) {
-        // past the last stage: push the offset beyond the resource's range (all
-        // ranges are < 2^31 bytes), so the load writes zeros; no branch
-        const uint32_t oob = kt < KT ? 0u : 0x80000000u;
-        const uint32_t kb = (uint32_t)kt * 128u + oob;
-        const uint32_t kbt = (uint32_t)kt * (uint32_t)(64 * Pdim * 2) + oob;
+    // past the last stage: push the offset beyond the resource's range (all
+    // ranges are < 2^31 bytes), so the load writes zeros; no branch
+    auto oob = [&](int kt) { return kt < KT ? 0u : 0x80000000u; };
+    // this wave's 8 loads of stage kt's weight tile / token tile
+    auto issue_w = [&](uint8_t* buf, int kt) {
+        const uint32_t kb = (uint32_t)kt * 128u + oob(kt);
+        const uint32_t kbt = (uint32_t)kt * (uint32_t)(64 * Pdim * 2) + oob(kt);
 #pragma unroll
-        for (int j = j0; j < j1; ++j) {
-            const int blk = 8 * wu + (j & 7);
-            uint32_t vo;
-            if (!P_KMAJOR && j < 8)
-                vo = ((j & 1) ? lane_off_t1 : lane_off_t0) + (uint32_t)blk * blk_stride_t + kbt;
-            else
-                vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ j) & 7)) << 4) + (uint32_t)blk * blk_stride + kb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 8 ? rp : rq,
-                                                     (lds_void*)(buf + (j < 8 ? 0 : kPipeTile) + blk * 1024), 16, vo,
-                                                     0, 0, 0);
+        for (int j = 0; j < 8; ++j) {
+            const int blk = 8 * wu + j;
+            const uint32_t vo =
+                P_KMAJOR ? lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ j) & 7)) << 4) + (uint32_t)blk * blk_stride + kb
+                         : ((j & 1) ? lane_off_t1 : lane_off_t0) + (uint32_t)blk * blk_stride_t + kbt;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
+        }
+    };
+    auto issue_t = [&](uint8_t* buf, int kt) {
+        const uint32_t kb = (uint32_t)kt * 128u + oob(kt);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int blk = 8 * wu + j;
+            const uint32_t vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ j) & 7)) << 4) + (uint32_t)blk * blk_stride + kb;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
     };
 
@@ -413,18 +420,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     bf16x8 fa[2][4], fb[2][4];
-    auto rd = [&](const uint8_t* buf, int kk, int s) {
+    auto rd = [&](const uint8_t* bw, const uint8_t* bt, int kk, int s) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             if constexpr (P_KMAJOR)
-                fa[s][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kmaj(wp * 128 + m * 32 + l32, 2 * kk + lh)));
+                fa[s][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(bw + kmaj(wp * 128 + m * 32 + l32, 2 * kk + lh)));
             else
-                fa[s][m] = pfrag_tr(buf, wp * 128 + m * 32, 16 * kk);  // p-contiguous weight tile
+                fa[s][m] = pfrag_tr(bw, wp * 128 + m * 32, 16 * kk);  // p-contiguous weight tile
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n)
-            fb[s][n] = as_bf16x8(
-                *reinterpret_cast<const u32x4*>(buf + kPipeTile + kmaj(wq * 128 + n * 32 + l32, 2 * kk + lh)));
+            fb[s][n] = as_bf16x8(*reinterpret_cast<const u32x4*>(bt + kmaj(wq * 128 + n * 32 + l32, 2 * kk + lh)));
     };
     auto mm = [&](int s) {
 #pragma unroll
@@ -440,45 +446,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
             if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // LDS DMA load
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if (i + 8 < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    constexpr int kLate = PLORA_DMA_SPLIT;  // loads of stage kt+1 issued during step 0 of stage kt
-    // stage kt in `cur`, stage kt+1 landing in `nxt`
-    auto stage = [&](uint8_t* cur, uint8_t* nxt, int kt) {
-        issue(nxt, kt + 1, 16 - kLate, 16);
-        rd(cur, 1, 1);
+    // Stage kt: token tile in tc, weight tile in wc; stage kt+1 landing in tn /
+    // wn; tf (free since the previous barrier) receives the token tile of stage
+    // kt+2.  In flight at the barrier: tokens kt+2 only (8 loads).
+    auto stage = [&](uint8_t* tc, uint8_t* wc, uint8_t* tn, uint8_t* wn, uint8_t* tf, int kt) {
+        issue_t(tf, kt + 2);
+        rd(wc, tc, 1, 1);
         mm(0);
-        sched(kLate);
-        rd(cur, 2, 0);
+        sched(8);
+        rd(wc, tc, 2, 0);
         mm(1);
         sched(0);
-        rd(cur, 3, 1);
+        rd(wc, tc, 3, 1);
         mm(0);
         sched(0);
-        wait_vmcnt<0>();  // stage kt+1 landed
-        lds_barrier();    // and every wave is done reading `cur`
+        wait_vmcnt<8>();  // stage kt+1 landed (tokens kt+2 may still be in flight)
+        lds_barrier();    // and every wave is done reading wc / tc
         __builtin_amdgcn_sched_barrier(0);
-        issue(cur, kt + 2, 0, 16 - kLate);
-        rd(nxt, 0, 0);
+        issue_w(wc, kt + 2);
+        rd(wn, tn, 0, 0);
         mm(1);
-        sched(16 - kLate);
+        sched(8);
     };
 
-    issue(g_stage0, 0, 0, 16);
-    issue(g_stage1, 1, 0, 16 - kLate);
-    wait_vmcnt<16 - kLate>();
+    issue_t(g_t0, 0);
+    issue_w(g_w0, 0);
+    issue_t(g_t1, 1);
+    issue_w(g_w1, 1);
+    wait_vmcnt<16>();
     lds_barrier();
-    rd(g_stage0, 0, 0);
-    for (int kt = 0; kt < KT; kt += 2) {  // KT is even
-        stage(g_stage0, g_stage1, kt);
-        stage(g_stage1, g_stage0, kt + 1);
+    rd(g_w0, g_t0, 0, 0);
+    int kt = 0;
+    for (; kt + 6 <= KT; kt += 6) {
+        stage(g_t0, g_w0, g_t1, g_w1, g_t2, kt);
+        stage(g_t1, g_w1, g_t2, g_w0, g_t0, kt + 1);
+        stage(g_t2, g_w0, g_t0, g_w1, g_t1, kt + 2);
+        stage(g_t0, g_w1, g_t1, g_w0, g_t2, kt + 3);
+        stage(g_t1, g_w0, g_t2, g_w1, g_t0, kt + 4);
+        stage(g_t2, g_w1, g_t0, g_w0, g_t1, kt + 5);
+    }
+    // KT is even: 0, 2 or 4 stages remain, continuing the same rotation
+    if (kt + 2 <= KT) {
+        stage(g_t0, g_w0, g_t1, g_w1, g_t2, kt);
+        stage(g_t1, g_w1, g_t2, g_w0, g_t0, kt + 1);
+    }
+    if (kt + 4 <= KT) {
+        stage(g_t2, g_w0, g_t0, g_w1, g_t1, kt + 2);
+        stage(g_t0, g_w1, g_t1, g_w0, g_t2, kt + 3);
     }
     wait_vmcnt<0>();
     lds_barrier();
 
-    if (a.lora && seg.n > 0) lora_expand(acc, a, seg, q0, p0, g_stage0, kBP * 2, g_stage0 + kPipeTile, g_stage1);
+    if (a.lora && seg.n > 0) lora_expand(acc, a, seg, q0, p0, g_t0, kBP * 2, g_w0, g_w1);
     store_tile(acc, a, q0, p0);
 }
 }  // namespace
