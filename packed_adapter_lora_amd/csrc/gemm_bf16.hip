@@ -206,6 +206,50 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Gemm
     }
 }
 
+// The same rounding and output, staged through LDS so that global stores are
+// whole 16-byte chunks of contiguous 256-byte row pieces (one instruction = 4
+// token rows x 256 bytes) instead of 8-byte pieces of 32 rows.  Each wave
+// writes its own 128 x 128 quarter into its own 32 KiB buffer `sb` (token rows
+// of 256 bytes); 8-byte slot s of row q is stored at slot s ^ (q % 32), which
+// keeps both the 8-byte writes (32 rows, one slot) and the 16-byte reads (one
+// row, 16 chunks) free of bank conflicts.  No workgroup barrier: a wave only
+// reads what it wrote.
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], const GemmArgs& a, int64_t q0, int64_t p0,
+                                               uint8_t* sb) {
+    bf16* __restrict__ O = static_cast<bf16*>(a.O);
+    const int64_t T = a.T, Pdim = a.Pdim;
+    const int l = lane_id(), w = wave_id();
+    const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int q = nt * 32 + l32;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 o;
+                o[0] = to_bf16(acc[mt][nt][4 * g + 0]);
+                o[1] = to_bf16(acc[mt][nt][4 * g + 1]);
+                o[2] = to_bf16(acc[mt][nt][4 * g + 2]);
+                o[3] = to_bf16(acc[mt][nt][4 * g + 3]);
+                const int slot = (mt * 8 + 2 * g + lh) ^ (q & 31);
+                *reinterpret_cast<bf16x4*>(sb + q * 256 + slot * 8) = o;
+            }
+        }
+    }
+    const int k = l & 15;
+    const int64_t pc = p0 + wp * 128 + 8 * k;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+        const int row = it * 4 + (l >> 4);
+        const int x = row & 31;
+        u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * 256 + ((k ^ (x >> 1)) << 4));
+        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int64_t t = q0 + wq * 128 + row;
+        if (t < T && pc < Pdim) *reinterpret_cast<u32x4*>(O + t * Pdim + pc) = v;
+    }
+}
+
 template <bool P_KMAJOR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTable seg) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
@@ -500,8 +544,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     wait_vmcnt<0>();
     lds_barrier();
 
-    if (a.lora && seg.n > 0) lora_expand(acc, a, seg, q0, p0, g_t0, kBP * 2, g_w0, g_w1);
-    store_tile(acc, a, q0, p0);
+    if (a.lora && seg.n > 0) {
+        lora_expand(acc, a, seg, q0, p0, g_t0, kBP * 2, g_w0, g_w1);
+        __syncthreads();  // the expand's LDS reads are done before the staging writes
+    }
+    store_tile_lds(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
 }
 }  // namespace
 
