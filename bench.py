@@ -85,7 +85,8 @@ def kernel_class(name):
     return None
 
 
-def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, workload, cmds):
+def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, workload, cmds,
+                    mfma_dir=None):
     """Summaries of rocprofv3 csv output: per-kernel time (--kernel-trace --stats) and
     HBM bytes per launch (FETCH_SIZE / WRITE_SIZE), each counter scaled by what it
     reads for a plain device copy of known size."""
@@ -139,6 +140,31 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_
     out["traffic_txt"] = "\n".join(lines) + "\n"
     out["traffic"] = traffic
     out["scales"] = (f_scale, w_scale)
+
+    # matrix-core utilisation per busy cycle and the clock the kernel ran at:
+    # SQ_VALU_MFMA_BUSY_CYCLES counts per SIMD (4 per CU), SQ_BUSY_CU_CYCLES per
+    # CU, GRBM_GUI_ACTIVE over the 8 XCDs; the clock divides one XCD's cycles by
+    # the kernel-trace duration of the same kernel
+    if mfma_dir and os.path.isdir(mfma_dir):
+        busy, cu, gui, n = (counter(mfma_dir, c) for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+                                                            "GRBM_GUI_ACTIVE", "SQ_INSTS_MFMA"))
+        avg_ns = {r["Name"]: float(r["AverageNs"]) for r in stats}
+        lines = ["# matrix-core busy fraction and effective clock, workload %s" % workload,
+                 "# command: " + cmds.get("mfma", ""), "# trace durations: " + cmds["trace"],
+                 "# mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES);"
+                 " clock = GRBM_GUI_ACTIVE / 8 XCDs / mean kernel-trace duration", "",
+                 "%-10s %12s %12s %12s %10s %10s" % ("class", "mfma_insts", "busy_cu_cyc", "cycles/xcd",
+                                                     "mfma_util", "clock_GHz")]
+        for name in sorted(busy):
+            cls = kernel_class(name)
+            if not cls:
+                continue
+            mean = lambda d: sum(d[name]) / len(d[name]) if name in d else float("nan")
+            b, c, g = mean(busy), mean(cu), mean(gui)
+            ns = avg_ns.get(name, float("nan"))
+            lines.append("%-10s %12.4g %12.4g %12.4g %10.3f %10.3f" % (cls, mean(n), c, g / 8, b / (4 * c),
+                                                                        g / 8 / ns))
+        out["mfma_txt"] = "\n".join(lines) + "\n"
     return out
 
 
@@ -271,11 +297,14 @@ def write_profiles(d, workload):
     cmds = json.load(open(os.path.join(d, "commands.json")))
     res = rocprof_summary(os.path.join(d, "trace"), os.path.join(d, "fetch"), os.path.join(d, "write"),
                           os.path.join(d, "copy_fetch"), os.path.join(d, "copy_write"), cmds["copy_bytes"],
-                          wl.name, cmds)
+                          wl.name, cmds, os.path.join(d, "mfma"))
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     open(os.path.join(prof, "kernels_%s_stats.txt" % wl.name), "w").write(res["stats"])
     open(os.path.join(prof, "kernels_%s_hbm_traffic.txt" % wl.name), "w").write(res["traffic_txt"])
+    if "mfma_txt" in res:
+        open(os.path.join(prof, "kernels_%s_mfma_clock.txt" % wl.name), "w").write(res["mfma_txt"])
+        print(res["mfma_txt"])
     src = {"gemm_fwd": "gemm_bf16.hip", "gemm_bwd": "gemm_bf16.hip", "shrink": "lora_bf16.hip",
            "wgrad": "lora_bf16.hip", "reduce": "lora_bf16.hip"}
     tj = {}
