@@ -75,7 +75,8 @@ def load_traffic(kernel, wl):
 
 KERNEL_CLASSES = (("gemm_lora_bf16_pipe<true>", "gemm_fwd"), ("gemm_lora_bf16_pipe<false>", "gemm_bwd"),
                   ("gemm_lora_bf16<true>", "gemm_fwd"), ("gemm_lora_bf16<false>", "gemm_bwd"),
-                  ("shrink_bf16", "shrink"), ("wgrad_reduce", "reduce"), ("wgrad_bf16", "wgrad"))
+                  ("shrink_bf16", "shrink"), ("wgrad_reduce", "reduce"), ("wgrad_bf16", "wgrad"),
+                  ("adamw_panel", "adamw"))
 
 
 def kernel_class(name):
@@ -216,9 +217,41 @@ def run_bench(wl, steps, warmup):
         n, ms = P.plora_profile_read(cls)
         kern[cls] = {"launches": n, "mean_ms": (ms / n) if n else 0.0, "ms_per_step": ms / steps}
     P.plora_profile_reset()
+    if wl.n_adapters:
+        kern["adamw"] = run_adamw(P, wl, d, dev, dA, dB, steps, warmup)
     del Y, dX, H, G, dA, dB, ws, dev
     torch.cuda.empty_cache()
     return (t1 - t0) / steps, kern, inp
+
+
+def run_adamw(P, wl, d, dev, dA, dB, steps, warmup):
+    """Per-adapter AdamW over the packed panels with the step's dA/dB, timed
+    apart from the operator step (HIP events per launch).  Algorithmic bytes
+    per element: read master, m, v, gradient (16) + write master, m, v (12) +
+    the operator copy (2 for bf16, 4 for fp32)."""
+    import torch
+    f32 = lambda t: t.to(torch.float32).contiguous()
+    PA, PB = f32(dev["A"]), f32(dev["B"])
+    mA, vA, mB, vB = (torch.zeros_like(t) for t in (PA, PA, PB, PB))
+    A, B = torch.empty_like(dev["A"]), torch.empty_like(dev["B"])
+    lr = [1e-3 * (1 + (i % 3)) for i in range(wl.n_adapters)]
+    for k in range(warmup):
+        P.plora_adamw_step(d, P.AdamwConfig(lr, [k + 1] * wl.n_adapters), PA, PB, mA, vA, mB, vB, dA, dB, A, B)
+    torch.cuda.synchronize()
+    P.plora_profile_reset()
+    P.plora_profile_enable(True)
+    for k in range(steps):
+        P.plora_adamw_step(d, P.AdamwConfig(lr, [warmup + k + 1] * wl.n_adapters), PA, PB, mA, vA, mB, vB, dA, dB,
+                           A, B)
+    torch.cuda.synchronize()
+    P.plora_profile_enable(False)
+    n, ms = P.plora_profile_read("adamw")
+    P.plora_profile_reset()
+    elems = wl.R * (wl.d_in + wl.d_out)
+    nbytes = elems * (28 + (2 if wl.dtype == "bf16" else 4))
+    per_call = ms / steps
+    return {"launches": n, "mean_ms": ms / n if n else 0.0, "ms_per_call": per_call, "bytes_per_call": nbytes,
+            "achieved_GBps": nbytes / (per_call * 1e-3) / 1e9 if per_call else 0.0}
 
 
 def run_loop_bench(wl, steps, warmup):
@@ -306,7 +339,7 @@ def write_profiles(d, workload):
         open(os.path.join(prof, "kernels_%s_mfma_clock.txt" % wl.name), "w").write(res["mfma_txt"])
         print(res["mfma_txt"])
     src = {"gemm_fwd": "gemm_bf16.hip", "gemm_bwd": "gemm_bf16.hip", "shrink": "lora_bf16.hip",
-           "wgrad": "lora_bf16.hip", "reduce": "lora_bf16.hip"}
+           "wgrad": "lora_bf16.hip", "reduce": "lora_bf16.hip", "adamw": "optim.hip"}
     tj = {}
     for cls, rec in res["traffic"].items():
         f = os.path.join(ROOT, "packed_adapter_lora_amd", "csrc", src[cls])
@@ -362,6 +395,7 @@ def main():
     wl = workloads.config(args.workload, n_adapters=args.adapters)
     log("workload %s: T=%d d_in=%d d_out=%d N=%d R=%d" % (wl.name, wl.T, wl.d_in, wl.d_out, wl.n_adapters, wl.R))
     sec, kern, inp = run_bench(wl, args.steps, args.warmup)
+    opt = kern.pop("adamw", None)
     tokens_per_s = wl.T / sec
     dom = max(("gemm_fwd", "gemm_bwd"), key=lambda k: kern[k]["mean_ms"])
     flops = gemm_flops(wl, dom)
@@ -397,12 +431,19 @@ def main():
         "whole_step_tflops": round(whole, 1),
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kern.items()},
     }
+    if opt:
+        # the per-adapter AdamW step over the packed panels, timed after (not in) the step above
+        out["optimizer"] = {"kernel": "adamw", "bound": "hbm", "ms_per_call": round(opt["ms_per_call"], 4),
+                            "bytes_per_call": opt["bytes_per_call"], "achieved": round(opt["achieved_GBps"], 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(opt["achieved_GBps"] / PEAK_HBM_GBS, 4)}
     print(json.dumps(out), flush=True)
 
     if args.sweep:
         for n in (2, 4, 8, 16, 32):
             w2 = workloads.config(args.workload, n_adapters=n)
             s2, k2, _ = run_bench(w2, args.steps, args.warmup)
+            k2.pop("adamw", None)
             s3 = run_loop_bench(w2, max(3, args.steps // 4), 2)
             print(json.dumps({"sweep": True, "workload": w2.name, "n_adapters": n, "tokens": w2.T,
                               "tokens_per_s": round(w2.T / s2, 1), "ms_per_step": round(s2 * 1e3, 4),

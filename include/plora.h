@@ -46,8 +46,10 @@
  * enqueues work only on `stream` (a hipStream_t; NULL means the null stream).
  * Host arrays in the descriptor are read during the call only.  Inputs are
  * never written.  Outputs (Y, H, dX, G, dA, dB) are overwritten, not
- * accumulated.  One training step calls plora_forward (writes H), then
- * plora_backward_dx (writes G), then plora_backward_dAdB (reads H and G).
+ * accumulated (plora_backward_dAdB_acc can accumulate dA and dB).  One
+ * training step calls plora_forward (writes H), then plora_backward_dx
+ * (writes G), then plora_backward_dAdB (reads H and G), then, to update the
+ * adapters, plora_adamw_step.
  *
  * Errors.  Every entry point returns PLORA_OK (0) or a negative plora_status.
  * All arguments are validated before anything is enqueued, so a call that
@@ -82,7 +84,8 @@ typedef enum {
     PLORA_ERR_DTYPE = -7,     /* dtype not a plora_dtype */
     PLORA_ERR_WORKSPACE = -8, /* workspace smaller than plora_workspace_bytes() */
     PLORA_ERR_ALIGN = -9,     /* a device pointer not 16-byte aligned */
-    PLORA_ERR_HIP = -10       /* a HIP runtime call or kernel launch failed */
+    PLORA_ERR_HIP = -10,      /* a HIP runtime call or kernel launch failed */
+    PLORA_ERR_HPARAM = -11    /* an optimizer hyper-parameter out of range */
 } plora_status;
 
 typedef enum { PLORA_F32 = 0, PLORA_BF16 = 1 } plora_dtype;
@@ -91,7 +94,8 @@ typedef enum { PLORA_F32 = 0, PLORA_BF16 = 1 } plora_dtype;
  *   n_adapters   N, 0..64.  N = 0 runs the frozen path only (Y = X W_m,
  *                dX = dY W_m^T); H, G, A, B may then be NULL.
  *   dtype        plora_dtype of X, W, A, B, Y, dY, dX.
- *   n_tokens     T >= 0.  T = 0 makes every call a no-op.
+ *   n_tokens     T >= 0.  With T = 0 plora_forward and plora_backward_dx do
+ *                nothing and plora_backward_dAdB writes dA = dB = 0.
  *   d_in, d_out  positive multiples of 8.
  *   seg_offsets  N+1 int64: o_0 = 0, non-decreasing, o_N = T; empty
  *                segments are allowed (that adapter gets dA_i = dB_i = 0).
@@ -128,6 +132,58 @@ int plora_backward_dAdB(const plora_desc* desc, const void* X, const void* dY, c
                         const float* G, float* dA, float* dB, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* plora_backward_dAdB with a choice of write mode.  accumulate = 0 behaves
+ * exactly like plora_backward_dAdB.  accumulate != 0 adds this call's
+ * gradients to dA and dB instead of overwriting them: each element becomes
+ * old + (s_i-scaled gradient of this call) in fp32, and adapters with no
+ * tokens in this call are left unchanged.  This sums the micro-batches of one
+ * optimizer step (gradient accumulation); the caller zeroes dA and dB, or
+ * passes accumulate = 0, for the first micro-batch. */
+int plora_backward_dAdB_acc(const plora_desc* desc, const void* X, const void* dY, const float* H,
+                            const float* G, float* dA, float* dB, void* workspace,
+                            size_t workspace_bytes, int accumulate, void* stream);
+
+/* Per-adapter AdamW over the packed adapter panels.
+ *
+ * The fine-tuning loop that trains the LoRA parameters uses AdamW with
+ * PyTorch's defaults (lr 1e-3, betas 0.9 / 0.999, eps 1e-8, weight decay
+ * 0.01) [LLM+LoRA微调加速技术原理解析 (m.youleyou.com), 5. 设定优化器和正则项];
+ * packed jobs differ in learning rate among other settings [PLoRA technical
+ * summary (gist.science, arXiv 2508.02932), 结果], so the learning rate, the
+ * weight decay and the step count are per adapter.  For every element of
+ * adapter i's rows (R_off[i] .. R_off[i]+r_i-1) of both panels, in fp32,
+ * with t = step[i] (decoupled weight decay; Loshchilov & Hutter, ICLR 2019):
+ *
+ *   p <- p (1 - lr_i wd_i)
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - (lr_i / (1 - beta1^t)) m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *
+ * The per-adapter factors (1 - lr wd, lr / (1 - beta1^t), 1 / sqrt(1 -
+ * beta2^t)) are formed in double on the host and rounded to fp32.
+ * step[i] = 0 leaves adapter i's parameters and moments untouched. */
+typedef struct {
+    float beta1;                /* 0 <= beta1 < 1 */
+    float beta2;                /* 0 <= beta2 < 1 */
+    float eps;                  /* finite, > 0 */
+    const float* lr;            /* HOST, N values: finite, >= 0 */
+    const float* weight_decay;  /* HOST, N values: finite, >= 0 */
+    const int64_t* step;        /* HOST, N values: >= 0 (1-based step count; 0 = skip) */
+} plora_adamw_config;
+
+/* One AdamW step for all adapters of `desc` (only n_adapters, ranks, dtype,
+ * d_in and d_out are used; the descriptor must still be valid).
+ *   PA, mA, vA  fp32 [R, d_in]: master copy of A and its moments, updated in place
+ *   PB, mB, vB  fp32 [R, d_out]: the same for B
+ *   dA, dB      fp32 gradients (layouts of A and B), read only
+ *   A, B        desc.dtype copies of the updated PA / PB for the operator
+ *               (bf16: round to nearest even; f32: a copy); either may be NULL
+ *               (not written) and, for f32, may be the same buffer as PA / PB.
+ * All device pointers 16-byte aligned.  N = 0 is a no-op. */
+int plora_adamw_step(const plora_desc* desc, const plora_adamw_config* cfg, float* PA, float* PB, float* mA,
+                     float* vA, float* mB, float* vB, const float* dA, const float* dB, void* A, void* B,
+                     void* stream);
+
 /* Number of fp32 elements of H (and of G): sum_i n_i r_i.  Returns 0 for an
  * invalid descriptor. */
 size_t plora_h_elems(const plora_desc* desc);
@@ -151,7 +207,7 @@ int plora_version(void);
 
 /* Kernel timing.  With profiling on, the library records a HIP event pair
  * on the call's stream around every kernel it launches (kernel classes:
- * "shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce").  After the caller has
+ * "shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce", "adamw").  After the caller has
  * synchronised the stream, plora_profile_read returns the number of launches
  * and their summed duration in milliseconds for one class.  Profiling is a
  * process-wide switch meant for benchmarks; it is not thread-safe. */

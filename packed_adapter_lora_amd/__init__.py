@@ -43,6 +43,17 @@ class plora_desc(ctypes.Structure):
     ]
 
 
+class plora_adamw_config(ctypes.Structure):
+    _fields_ = [
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("lr", ctypes.POINTER(ctypes.c_float)),
+        ("weight_decay", ctypes.POINTER(ctypes.c_float)),
+        ("step", ctypes.POINTER(ctypes.c_int64)),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libplora.so is not built (run: python -m packed_adapter_lora_amd.build)")
@@ -53,6 +64,9 @@ def _load():
         "plora_forward": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, fp, vp]),
         "plora_backward_dx": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, fp, vp]),
         "plora_backward_dAdB": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]),
+        "plora_backward_dAdB_acc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, ctypes.c_int,
+                                                   vp]),
+        "plora_adamw_step": (ctypes.c_int, [dp, ctypes.POINTER(plora_adamw_config)] + [vp] * 11),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
         "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
         "plora_validate": (ctypes.c_int, [dp]),
@@ -170,7 +184,7 @@ def plora_backward_dx(desc: Desc, dY, W, A, B, dX, G, stream=None):
                                   _stream(stream)))
 
 
-def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=None):
+def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=None, accumulate=False):
     T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
     e = _elt(desc)
     he = plora_h_elems(desc)
@@ -182,8 +196,47 @@ def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=
         nbytes = workspace.numel() * workspace.element_size()
     elif isinstance(workspace, int):
         nbytes = plora_workspace_bytes(desc)
-    _check(_lib.plora_backward_dAdB(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA), _addr(dB),
-                                    _addr(workspace), nbytes, _stream(stream)))
+    _check(_lib.plora_backward_dAdB_acc(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA), _addr(dB),
+                                        _addr(workspace), nbytes, 1 if accumulate else 0, _stream(stream)))
+
+
+class AdamwConfig:
+    """Host-side AdamW settings for plora_adamw_step: per-adapter learning rate,
+    weight decay and step count (0 = skip the adapter), shared betas and eps.
+    Defaults are PyTorch's AdamW defaults."""
+
+    def __init__(self, lr, step, weight_decay=0.01, beta1=0.9, beta2=0.999, eps=1e-8):
+        n = len(step)
+        wd = [weight_decay] * n if np.isscalar(weight_decay) else list(weight_decay)
+        lr = [lr] * n if np.isscalar(lr) else list(lr)
+        if len(lr) != n or len(wd) != n:
+            raise ValueError("lr, weight_decay and step need one value per adapter")
+        self.lr = np.ascontiguousarray(lr, dtype=np.float32)
+        self.wd = np.ascontiguousarray(wd, dtype=np.float32)
+        self.step = np.ascontiguousarray(step, dtype=np.int64)
+        self.c = plora_adamw_config(beta1, beta2, eps,
+                                    self.lr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                    self.wd.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                    self.step.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def plora_adamw_step(desc: Desc, cfg: AdamwConfig, PA, PB, mA, vA, mB, vB, dA, dB, A=None, B=None, stream=None):
+    """One per-adapter AdamW step over the packed panels (see plora.h)."""
+    R, di, do = desc.R, int(desc.c.d_in), int(desc.c.d_out)
+    if len(cfg.step) != int(desc.c.n_adapters):
+        raise ValueError("AdamW configuration has %d adapters, descriptor %d" % (len(cfg.step), desc.c.n_adapters))
+    for n, t, shp in (("PA", PA, (R, di)), ("mA", mA, (R, di)), ("vA", vA, (R, di)), ("dA", dA, (R, di)),
+                      ("PB", PB, (R, do)), ("mB", mB, (R, do)), ("vB", vB, (R, do)), ("dB", dB, (R, do))):
+        _check_tensor(n, t, shp, "float32")
+    e = _elt(desc)
+    for n, t, shp in (("A", A, (R, di)), ("B", B, (R, do))):
+        if t is not None:
+            _check_tensor(n, t, shp, e)
+    _check(_lib.plora_adamw_step(desc.ref(), cfg.ref(), _addr(PA), _addr(PB), _addr(mA), _addr(vA), _addr(mB),
+                                 _addr(vB), _addr(dA), _addr(dB), _addr(A), _addr(B), _stream(stream)))
 
 
 def plora_h_elems(desc: Desc) -> int:

@@ -6,6 +6,7 @@
 // is synchronised.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -94,6 +95,7 @@ const char* plora_status_string(int s) {
         case PLORA_ERR_WORKSPACE: return "PLORA_ERR_WORKSPACE";
         case PLORA_ERR_ALIGN: return "PLORA_ERR_ALIGN";
         case PLORA_ERR_HIP: return "PLORA_ERR_HIP";
+        case PLORA_ERR_HPARAM: return "PLORA_ERR_HPARAM";
         default: return "PLORA_ERR_UNKNOWN";
     }
 }
@@ -198,6 +200,11 @@ int plora_backward_dx(const plora_desc* d, const void* dY, const void* W, const 
 
 int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, const float* H, const float* G, float* dA,
                         float* dB, void* ws, size_t ws_bytes, void* stream) {
+    return plora_backward_dAdB_acc(d, X, dY, H, G, dA, dB, ws, ws_bytes, 0, stream);
+}
+
+int plora_backward_dAdB_acc(const plora_desc* d, const void* X, const void* dY, const float* H, const float* G,
+                            float* dA, float* dB, void* ws, size_t ws_bytes, int accumulate, void* stream) {
     try {
         int rc = check_common(d);
         if (rc) return rc;
@@ -209,10 +216,11 @@ int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, cons
         SegTable s;
         build_segtable(d, &s);
         const hipStream_t st = static_cast<hipStream_t>(stream);
+        const int32_t acc = accumulate ? 1 : 0;
         hipError_t e = hipSuccess;
         if (d->dtype == PLORA_F32) {
-            const WgradArgs wb{dY, H, dB, nullptr, d->d_out};
-            const WgradArgs wa{X, G, dA, nullptr, d->d_in};
+            const WgradArgs wb{dY, H, dB, nullptr, d->d_out, acc};
+            const WgradArgs wa{X, G, dA, nullptr, d->d_in, acc};
             e = timed("wgrad", st, [&] { return launch_wgrad_f32(wb, s, st); });
             if (e != hipSuccess) return hip_fail(e, "wgrad launch");
             e = timed("wgrad", st, [&] { return launch_wgrad_f32(wa, s, st); });
@@ -232,8 +240,8 @@ int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, cons
         float* part_b = wsb ? reinterpret_cast<float*>(wsb + wl.part_b) : nullptr;
         __bf16* g_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_g) : nullptr;
         __bf16* h_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_h) : nullptr;
-        const WgradArgs wb{dY, H, dB, part_b, d->d_out};
-        const WgradArgs wa{X, G, dA, part_a, d->d_in};
+        const WgradArgs wb{dY, H, dB, part_b, d->d_out, acc};
+        const WgradArgs wa{X, G, dA, part_a, d->d_in, acc};
         e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st); });
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
         e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
@@ -242,6 +250,61 @@ int plora_backward_dAdB(const plora_desc* d, const void* X, const void* dY, cons
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
         e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
         if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_adamw_step(const plora_desc* d, const plora_adamw_config* cfg, float* PA, float* PB, float* mA, float* vA,
+                     float* mB, float* vB, const float* dA, const float* dB, void* A, void* B, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_adapters == 0) return PLORA_OK;
+        if (!cfg || !cfg->lr || !cfg->weight_decay || !cfg->step)
+            return fail(PLORA_ERR_NULL, "the AdamW configuration and its lr, weight_decay and step arrays are required");
+        const float b1 = cfg->beta1, b2 = cfg->beta2, eps = cfg->eps;
+        if (!(b1 >= 0.0f && b1 < 1.0f) || !(b2 >= 0.0f && b2 < 1.0f))
+            return fail(PLORA_ERR_HPARAM, "betas must lie in [0, 1)");
+        if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(PLORA_ERR_HPARAM, "eps must be finite and > 0");
+        for (int i = 0; i < d->n_adapters; ++i) {
+            if (!(cfg->lr[i] >= 0.0f) || !std::isfinite(cfg->lr[i]))
+                return fail(PLORA_ERR_HPARAM, "lr[" + std::to_string(i) + "] must be finite and >= 0");
+            if (!(cfg->weight_decay[i] >= 0.0f) || !std::isfinite(cfg->weight_decay[i]))
+                return fail(PLORA_ERR_HPARAM, "weight_decay[" + std::to_string(i) + "] must be finite and >= 0");
+            if (cfg->step[i] < 0) return fail(PLORA_ERR_HPARAM, "step[" + std::to_string(i) + "] must be >= 0");
+        }
+        if (!PA || !PB || !mA || !vA || !mB || !vB || !dA || !dB)
+            return fail(PLORA_ERR_NULL, "PA, PB, mA, vA, mB, vB, dA and dB are required");
+        if (misaligned(PA) || misaligned(PB) || misaligned(mA) || misaligned(vA) || misaligned(mB) ||
+            misaligned(vB) || misaligned(dA) || misaligned(dB) || misaligned(A) || misaligned(B))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        AdamwTable t{};
+        t.n = d->n_adapters;
+        t.roff[0] = 0;
+        for (int i = 0; i < t.n; ++i) {
+            t.roff[i + 1] = t.roff[i] + d->ranks[i];
+            const int64_t k = cfg->step[i];
+            t.active[i] = k > 0;
+            const double lr = cfg->lr[i], wd = cfg->weight_decay[i];
+            t.decay[i] = (float)(1.0 - lr * wd);
+            t.step_size[i] = k > 0 ? (float)(lr / (1.0 - std::pow((double)b1, (double)k))) : 0.0f;
+            t.rs_bc2[i] = k > 0 ? (float)(1.0 / std::sqrt(1.0 - std::pow((double)b2, (double)k))) : 0.0f;
+        }
+        t.beta1 = b1;
+        t.one_minus_beta1 = (float)(1.0 - (double)b1);
+        t.beta2 = b2;
+        t.one_minus_beta2 = (float)(1.0 - (double)b2);
+        t.eps = eps;
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const int32_t bf = d->dtype == PLORA_BF16 ? 1 : 0;
+        const AdamwArgs aa{PA, mA, vA, dA, A, bf, d->d_in};
+        const AdamwArgs ab{PB, mB, vB, dB, B, bf, d->d_out};
+        hipError_t e = timed("adamw", st, [&] { return launch_adamw(aa, t, st); });
+        if (e != hipSuccess) return hip_fail(e, "adamw launch");
+        e = timed("adamw", st, [&] { return launch_adamw(ab, t, st); });
+        if (e != hipSuccess) return hip_fail(e, "adamw launch");
         return PLORA_OK;
     } catch (...) {
         return fail(PLORA_ERR_HIP, "unexpected exception");

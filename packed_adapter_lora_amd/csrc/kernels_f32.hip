@@ -103,11 +103,13 @@ __global__ __launch_bounds__(256) void wgrad_f32(WgradArgs a, SegTable seg) {
     const int r = seg.rank[i];
     const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (c >= a.D) return;
+    if (a.accumulate && seg.off[i + 1] == seg.off[i]) return;  // no tokens: leave the rows alone
     const float* __restrict__ Q = static_cast<const float*>(a.Q);
     const float* f = a.F + seg.hoff[i];
     float s = 0.0f;
     for (int64_t t = seg.off[i]; t < seg.off[i + 1]; ++t) s = fmaf(f[(t - seg.off[i]) * r + j], Q[t * a.D + c], s);
-    a.out[(int64_t)g * a.D + c] = seg.scale[i] * s;
+    const int64_t o = (int64_t)g * a.D + c;
+    a.out[o] = a.accumulate ? a.out[o] + seg.scale[i] * s : seg.scale[i] * s;
 }
 
 }  // namespace

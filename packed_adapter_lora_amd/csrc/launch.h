@@ -40,6 +40,7 @@ struct WgradArgs {
     float* out;        // dA or dB, [R][D]
     float* part;       // fp32 partials (adapters split over several chunks)
     int64_t D;
+    int32_t accumulate;  // nonzero: out += result (adapters without tokens untouched)
 };
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);
@@ -51,6 +52,30 @@ hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradP
 hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, __bf16* fhi, __bf16* flo,
                                   hipStream_t st);
 hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);
+
+// Per-adapter AdamW over one packed panel [R][D] (fp32 master P, moments m, v,
+// gradient g; optional operator copy `out` of dtype out_dtype).  The factors
+// are per adapter: decay = 1 - lr wd, step_size = lr / (1 - beta1^t),
+// rs_bc2 = 1 / sqrt(1 - beta2^t); active = 0 skips the adapter.
+struct AdamwTable {
+    int32_t n;
+    int32_t roff[kMaxN + 1];
+    int32_t active[kMaxN];
+    float decay[kMaxN];
+    float step_size[kMaxN];
+    float rs_bc2[kMaxN];
+    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps;
+};
+struct AdamwArgs {
+    float* P;
+    float* m;
+    float* v;
+    const float* g;
+    void* out;          // nullptr: not written
+    int32_t out_bf16;   // 1: bf16 (round to nearest even), 0: fp32
+    int64_t D;
+};
+hipError_t launch_adamw(const AdamwArgs& a, const AdamwTable& t, hipStream_t st);
 
 hipError_t launch_gemm_f32(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);
 hipError_t launch_shrink_f32(const ShrinkArgs& a, const SegTable& s, hipStream_t st);

@@ -351,7 +351,11 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                if (j < r) dst[(int64_t)j * D + c] = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+                if (j < r) {
+                    float val = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+                    if (direct && a.accumulate) val += dst[(int64_t)j * D + c];
+                    dst[(int64_t)j * D + c] = val;
+                }
             }
         }
     }
@@ -507,18 +511,23 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                if (j < r) dst[(int64_t)j * D + c] = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+                if (j < r) {
+                    float val = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
+                    if (direct && a.accumulate) val += dst[(int64_t)j * D + c];
+                    dst[(int64_t)j * D + c] = val;
+                }
             }
         }
     }
 }
 
 // out rows of adapters whose tokens span 0 or >= 2 chunks:
-// out = s_i * sum_u partial[u] in chunk order (0 for an empty adapter).
+// out = s_i * sum_u partial[u] in chunk order (0 for an empty adapter), or
+// out += that when accumulating (an empty adapter is then left alone).
 __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, WgradPlan plan) {
     const int i = (int)blockIdx.y;
     const int nch = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
-    if (nch == 1) return;
+    if (nch == 1 || (nch == 0 && a.accumulate)) return;
     const int64_t n = (int64_t)seg.rank[i] * a.D;  // multiple of 8
     const float sc = seg.scale[i];
     float* __restrict__ out = a.out + (int64_t)seg.roff[i] * a.D;
@@ -526,7 +535,9 @@ __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, W
     for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 1024) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         for (int u = 0; u < nch; ++u) s += *reinterpret_cast<const f32x4*>(part + (int64_t)u * n + e);
-        *reinterpret_cast<f32x4*>(out + e) = s * sc;
+        f32x4 o = s * sc;
+        if (a.accumulate) o += *reinterpret_cast<const f32x4*>(out + e);
+        *reinterpret_cast<f32x4*>(out + e) = o;
     }
 }
 

@@ -176,3 +176,59 @@ int main() {
     # dB (2048-token chunks): adapter 3 has 3 chunks
     assert out[8] == str(1 + 0 + 1 + 3) and out[9] == str(3 * 64 * 14336)
     assert out[10] == "64" and float(out[11]) == 2.0 and float(out[12]) == 2.0
+
+
+def test_status_string_hparam(P):
+    assert P.plora_status_string(-11) == "PLORA_ERR_HPARAM"
+
+
+def test_adamw_validation(P):
+    d = desc(P, counts=(3, 0, 5), ranks=(4, 8, 16))
+    lib = P._lib
+    ptrs = [0x1000 * (k + 1) for k in range(8)]  # never dereferenced: every case fails or is a no-op first
+
+    def call(cfg, ps=ptrs, A=None, B=None, dd=d):
+        return lib.plora_adamw_step(dd.ref(), cfg.ref() if cfg is not None else None, *ps, A, B, None)
+
+    assert call(None) == -1
+    assert call(P.AdamwConfig([1e-3] * 3, [1, 1, 1], beta1=1.0)) == -11
+    assert call(P.AdamwConfig([1e-3] * 3, [1, 1, 1], beta2=-0.1)) == -11
+    assert call(P.AdamwConfig([1e-3] * 3, [1, 1, 1], eps=0.0)) == -11
+    assert call(P.AdamwConfig([1e-3, float("nan"), 1e-3], [1, 1, 1])) == -11
+    assert call(P.AdamwConfig([1e-3] * 3, [1, 1, 1], weight_decay=[0.0, -1.0, 0.0])) == -11
+    assert call(P.AdamwConfig([1e-3] * 3, [1, -2, 1])) == -11
+    assert "step[1]" in P.plora_last_error()
+    ok = P.AdamwConfig([1e-3] * 3, [1, 0, 2])
+    assert call(ok, ps=[None] + ptrs[1:]) == -1
+    assert call(ok, ps=ptrs[:3] + [0x3008] + ptrs[4:]) == -9
+    assert call(ok, A=0x7001) == -9
+    bad = desc(P, ranks=(4, 0, 16))
+    assert call(ok, dd=bad) == -3
+    n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
+    assert lib.plora_adamw_step(n0.ref(), None, *([None] * 10), None) == 0
+
+
+def test_adamw_python_checks(P):
+    torch = pytest.importorskip("torch")
+    d = desc(P, counts=(3, 0, 5), ranks=(4, 8, 16), d_in=64, d_out=32)
+    f = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        P.AdamwConfig([1e-3, 1e-3], [1, 1, 1])
+    with pytest.raises(ValueError):  # wrong number of adapters
+        P.plora_adamw_step(d, P.AdamwConfig(1e-3, [1, 1]), f(28, 64), f(28, 32), f(28, 64), f(28, 64), f(28, 32),
+                           f(28, 32), f(28, 64), f(28, 32))
+    with pytest.raises(ValueError):  # PB with the shape of A
+        P.plora_adamw_step(d, P.AdamwConfig(1e-3, [1, 1, 1]), f(28, 64), f(28, 64), f(28, 64), f(28, 64), f(28, 32),
+                           f(28, 32), f(28, 64), f(28, 32))
+
+
+def test_dadb_acc_error_paths(P):
+    lib = P._lib
+    bad = desc(P, ranks=(4, 0, 16))
+    assert lib.plora_backward_dAdB_acc(bad.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None, 0, 1,
+                                       None) == -3
+    big = desc(P, counts=(5000, 1, 0), ranks=(64, 8, 16), d_in=4096, d_out=16384)
+    assert lib.plora_backward_dAdB_acc(big.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 16, 1,
+                                       None) == -8
+    n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
+    assert lib.plora_backward_dAdB_acc(n0.ref(), None, None, None, None, None, None, None, 0, 1, None) == 0

@@ -249,3 +249,18 @@ def sample_rows(wl: Workload, per_segment: int = 4, seed: int = 99) -> np.ndarra
             rows.update([m - 1, m])
         rows.update(rng.integers(a, b, size=min(per_segment, b - a)).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < wl.T), dtype=np.int64)
+
+
+def optimizer_state(wl: Workload, seed: int) -> dict:
+    """fp32 optimizer inputs for the packed panels (N(0, v) names the variance):
+    master weights PA/PB (the adapters' own draws, full fp32), first moments
+    mA/mB ~ N(0, 1e-6), second moments vA/vB = squares of N(0, 1e-6) draws,
+    gradients dA/dB ~ N(0, 1e-4)."""
+    R, di, do = wl.R, wl.d_in, wl.d_out
+    base = make_inputs(custom(di, do, [0] * wl.n_adapters, wl.ranks, wl.alphas, "f32", seed), which=("A", "B"))
+    out = {"PA": base["A"], "PB": base["B"]}
+    for k, tid, d in (("A", 20, di), ("B", 21, do)):
+        out["m" + k] = draw(seed, tid, (R, d), 1e-3, "f32")
+        out["v" + k] = np.square(draw(seed, tid + 10, (R, d), 1e-3, "f32"))
+        out["d" + k] = draw(seed, tid + 20, (R, d), 1e-2, "f32")
+    return out
