@@ -67,6 +67,16 @@ def _load():
         "plora_backward_dAdB_acc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                                    vp]),
         "plora_adamw_step": (ctypes.c_int, [dp, ctypes.POINTER(plora_adamw_config)] + [vp] * 11),
+        "plora_rmsnorm_fwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                             vp]),
+        "plora_rmsnorm_bwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64] + [vp] * 9),
+        "plora_rope": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_float, ctypes.c_int,
+                                      vp, vp]),
+        "plora_swiglu_fwd": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
+        "plora_swiglu_bwd": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp, vp, vp]),
+        "plora_add": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
+        "plora_attention_fwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 6),
+        "plora_attention_bwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 11),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
         "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
         "plora_validate": (ctypes.c_int, [dp]),
@@ -276,3 +286,88 @@ def plora_profile_read(kernel_class: str):
 
 def plora_profile_reset():
     _lib.plora_profile_reset()
+
+
+# ---------------------------------------------------------------------------
+# Decoder-block kernels (include/plora_block.h).  Tensors are bf16 torch
+# tensors; sequence tables are host int64 arrays of n_seq + 1 offsets.
+# ---------------------------------------------------------------------------
+
+def _seq(seq_offsets):
+    off = np.ascontiguousarray(seq_offsets, dtype=np.int64)
+    return off, len(off) - 1, off.ctypes.data
+
+
+def _bf16(name, t, shape=None):
+    _check_tensor(name, t, shape if shape is not None else tuple(t.shape), "bfloat16")
+
+
+def plora_rmsnorm_fwd(x, w, h, rstd, res=None, xs_out=None, eps=1e-5, stream=None):
+    T, D = x.shape
+    for n, t in (("x", x), ("h", h), ("res", res), ("xs_out", xs_out)):
+        if t is not None:
+            _bf16(n, t, (T, D))
+    _bf16("w", w, (D,))
+    _check_tensor("rstd", rstd, (T,), "float32")
+    _check(_lib.plora_rmsnorm_fwd(T, D, _addr(x), _addr(res), _addr(w), eps, _addr(xs_out), _addr(h), _addr(rstd),
+                                  _stream(stream)))
+
+
+def plora_rmsnorm_bwd(dys, x, w, rstd, dx, dres=None, stream=None):
+    T, D = x.shape
+    dys = list(dys) + [None] * (3 - len(dys))
+    for n, t in (("dy0", dys[0]), ("dy1", dys[1]), ("dy2", dys[2]), ("x", x), ("dres", dres), ("dx", dx)):
+        if t is not None:
+            _bf16(n, t, (T, D))
+    _bf16("w", w, (D,))
+    _check_tensor("rstd", rstd, (T,), "float32")
+    _check(_lib.plora_rmsnorm_bwd(T, D, _addr(dys[0]), _addr(dys[1]), _addr(dys[2]), _addr(x), _addr(w), _addr(rstd),
+                                  _addr(dres), _addr(dx), _stream(stream)))
+
+
+def plora_rope(x, seq_offsets, heads, base=500000.0, inverse=False, stream=None):
+    off, n, p = _seq(seq_offsets)
+    _bf16("x", x, (int(off[-1]), heads * 128))
+    _check(_lib.plora_rope(int(off[-1]), heads, n, p, base, 1 if inverse else 0, _addr(x), _stream(stream)))
+
+
+def plora_swiglu_fwd(g, u, a, stream=None):
+    for n, t in (("g", g), ("u", u), ("a", a)):
+        _bf16(n, t, tuple(g.shape))
+    _check(_lib.plora_swiglu_fwd(g.numel(), _addr(g), _addr(u), _addr(a), _stream(stream)))
+
+
+def plora_swiglu_bwd(da, g, u, dg, du, stream=None):
+    for n, t in (("da", da), ("g", g), ("u", u), ("dg", dg), ("du", du)):
+        _bf16(n, t, tuple(g.shape))
+    _check(_lib.plora_swiglu_bwd(g.numel(), _addr(da), _addr(g), _addr(u), _addr(dg), _addr(du), _stream(stream)))
+
+
+def plora_add(x, y, out, stream=None):
+    for n, t in (("x", x), ("y", y), ("out", out)):
+        _bf16(n, t, tuple(x.shape))
+    _check(_lib.plora_add(x.numel(), _addr(x), _addr(y), _addr(out), _stream(stream)))
+
+
+def plora_attention_fwd(q, k, v, o, lse, seq_offsets, n_q, n_kv, stream=None):
+    off, n, p = _seq(seq_offsets)
+    T = int(off[-1])
+    _bf16("q", q, (T, n_q * 128))
+    _bf16("k", k, (T, n_kv * 128))
+    _bf16("v", v, (T, n_kv * 128))
+    _bf16("o", o, (T, n_q * 128))
+    _check_tensor("lse", lse, (n_q, T), "float32")
+    _check(_lib.plora_attention_fwd(n, p, n_q, n_kv, _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse),
+                                    _stream(stream)))
+
+
+def plora_attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, seq_offsets, n_q, n_kv, stream=None):
+    off, n, p = _seq(seq_offsets)
+    T = int(off[-1])
+    for nm, t, hh in (("q", q, n_q), ("k", k, n_kv), ("v", v, n_kv), ("o", o, n_q), ("dO", dO, n_q), ("dq", dq, n_q),
+                      ("dk", dk, n_kv), ("dv", dv, n_kv)):
+        _bf16(nm, t, (T, hh * 128))
+    _check_tensor("lse", lse, (n_q, T), "float32")
+    _check_tensor("delta", delta, (n_q, T), "float32")
+    _check(_lib.plora_attention_bwd(n, p, n_q, n_kv, _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dO),
+                                    _addr(dq), _addr(dk), _addr(dv), _addr(delta), _stream(stream)))

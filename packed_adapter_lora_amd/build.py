@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libplora.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["api.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip", "optim.hip"]
+HIP_SOURCES = ["api.hip", "api_block.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip", "optim.hip",
+               "block.hip", "attention.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

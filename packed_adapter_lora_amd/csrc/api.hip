@@ -13,12 +13,12 @@
 #include <string>
 #include <vector>
 
+#include "api_util.h"
 #include "launch.h"
 #include "plan.h"
 #include "plora.h"
 
 namespace plora {
-namespace {
 
 thread_local std::string g_last_error;
 
@@ -31,19 +31,7 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(PLORA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-
-// ---- kernel timing (process-wide switch for benchmarks) ----------------------
-struct ProfRec {
-    std::string cls;
-    hipEvent_t a, b;
-};
-struct Prof {
-    bool on = false;
-    std::vector<ProfRec> recs;
-    std::vector<hipEvent_t> pool;
-    std::mutex mu;
-} g_prof;
+Prof g_prof;
 
 hipEvent_t take_event() {
     if (!g_prof.pool.empty()) {
@@ -56,17 +44,7 @@ hipEvent_t take_event() {
     return e;
 }
 
-template <class Fn>
-hipError_t timed(const char* cls, hipStream_t st, Fn&& fn) {
-    if (!g_prof.on) return fn();
-    std::lock_guard<std::mutex> lk(g_prof.mu);
-    hipEvent_t a = take_event(), b = take_event();
-    if (a) (void)hipEventRecord(a, st);
-    const hipError_t e = fn();
-    if (b) (void)hipEventRecord(b, st);
-    if (a && b) g_prof.recs.push_back({cls, a, b});
-    return e;
-}
+namespace {
 
 int check_common(const plora_desc* d) {
     const char* why = "";

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "plora.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,15 +23,19 @@ def P():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(plora_[a-z_A-Z0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(plora_[a-z_A-Z0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
-              "plora_workspace_bytes", "plora_status_string", "plora_last_error", "plora_version"):
+              "plora_workspace_bytes", "plora_status_string", "plora_last_error", "plora_version",
+              "plora_backward_dAdB_acc", "plora_adamw_step", "plora_rmsnorm_fwd", "plora_rmsnorm_bwd", "plora_rope",
+              "plora_swiglu_fwd", "plora_swiglu_bwd", "plora_add", "plora_attention_fwd", "plora_attention_bwd"):
         assert n in names
 
 

@@ -1,0 +1,144 @@
+"""GPU parity of the decoder-block kernels through the C ABI against the fp64
+oracle (oracle/block.py), on the same bf16 inputs.
+
+Tolerances: each kernel rounds its outputs to bf16 once (relative 2^-9), and
+attention additionally rounds the softmax weights to bf16 before the product
+with V, so outputs are compared blockwise at 1e-2 (rmsnorm, rope, swiglu,
+add) and 2e-2 (attention), with the same two-part criterion as the operator
+(Frobenius and elementwise)."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import block as OB
+from parity_utils import check_block, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import packed_adapter_lora_amd as P  # raises if libplora.so is missing
+    return P
+
+
+def bf(shape, seed, tid, std=1.0):
+    """Seeded bf16-representable fp32 values."""
+    return workloads.draw(seed, tid, shape, std, "bf16")
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+
+
+def dev32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda")
+
+
+def rnd(a):
+    """Round to bf16 (what a kernel stores)."""
+    return workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(np.asarray(a, np.float32))).reshape(np.shape(a))
+
+
+@pytest.mark.parametrize("D", [4096, 328])
+def test_rmsnorm_fwd(P, D):
+    import torch
+    T = 77
+    x, r, w = bf((T, D), 61, 1), bf((T, D), 61, 2, 0.5), bf((1, D), 61, 3)[0]
+    h = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    xs = torch.full_like(h, float("nan"))
+    rstd = torch.full((T,), float("nan"), dtype=torch.float32, device="cuda")
+    P.plora_rmsnorm_fwd(dev(x), dev(w), h, rstd, res=dev(r), xs_out=xs, eps=1e-5)
+    torch.cuda.synchronize()
+    xs_ref = x.astype(np.float64) + r  # exact in fp64; the kernel stores it rounded to bf16
+    np.testing.assert_array_equal(host(xs), rnd(xs_ref))
+    h_ref, rstd_ref = OB.rmsnorm_fwd(rnd(xs_ref), w, 1e-5)
+    check_block(host(h), h_ref, 1e-2, "h")
+    np.testing.assert_allclose(host(rstd), rstd_ref, rtol=1e-5)
+    # without the residual
+    P.plora_rmsnorm_fwd(dev(x), dev(w), h, rstd, eps=1e-5)
+    torch.cuda.synchronize()
+    check_block(host(h), OB.rmsnorm_fwd(x, w, 1e-5)[0], 1e-2, "h (no residual)")
+
+
+def test_rmsnorm_bwd(P):
+    import torch
+    T, D = 65, 4096
+    x, w = bf((T, D), 62, 1), bf((1, D), 62, 2)[0]
+    dys = [bf((T, D), 62, 3 + k, 0.1) for k in range(3)]
+    dres = bf((T, D), 62, 7, 0.1)
+    _, rstd = OB.rmsnorm_fwd(x, w, 1e-5)
+    rstd32 = rstd.astype(np.float32)
+    dx = torch.full((T, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    P.plora_rmsnorm_bwd([dev(d) for d in dys], dev(x), dev(w), dev32(rstd32), dx, dres=dev(dres))
+    torch.cuda.synchronize()
+    ref = dres + OB.rmsnorm_bwd(dys[0].astype(np.float64) + dys[1] + dys[2], x, w, rstd32.astype(np.float64))
+    check_block(host(dx), ref, 1e-2, "dx")
+    P.plora_rmsnorm_bwd([dev(dys[0])], dev(x), dev(w), dev32(rstd32), dx)
+    torch.cuda.synchronize()
+    check_block(host(dx), OB.rmsnorm_bwd(dys[0], x, w, rstd32.astype(np.float64)), 1e-2, "dx (one gradient)")
+
+
+@pytest.mark.parametrize("inverse", [False, True])
+def test_rope(P, inverse):
+    import torch
+    offs = [0, 1, 300, 300, 1100]
+    T, heads = offs[-1], 8
+    x = bf((T, heads * 128), 63, 1)
+    xd = dev(x)
+    P.plora_rope(xd, offs, heads, base=500000.0, inverse=inverse)
+    torch.cuda.synchronize()
+    pos = OB.positions_of(offs)
+    ref = OB.rope_bwd(x, pos) if inverse else OB.rope_fwd(x, pos)
+    check_block(host(xd), ref, 1e-2, "rope")
+
+
+def test_swiglu_and_add(P):
+    import torch
+    n = (37, 1000)
+    g, u, da = bf(n, 64, 1, 3.0), bf(n, 64, 2), bf(n, 64, 3)
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    P.plora_swiglu_fwd(dev(g), dev(u), a)
+    dg, du = torch.empty_like(a), torch.empty_like(a)
+    P.plora_swiglu_bwd(dev(da), dev(g), dev(u), dg, du)
+    out = torch.empty_like(a)
+    P.plora_add(dev(g), dev(u), out)
+    torch.cuda.synchronize()
+    check_block(host(a), OB.swiglu_fwd(g, u), 1e-2, "swiglu")
+    rg, ru = OB.swiglu_bwd(da, g, u)
+    check_block(host(dg), rg, 1e-2, "dg")
+    check_block(host(du), ru, 1e-2, "du")
+    np.testing.assert_array_equal(host(out), rnd(g.astype(np.float64) + u))
+
+
+def attn_inputs(offs, n_q, n_kv, seed):
+    T = offs[-1]
+    return bf((T, n_q * 128), seed, 1), bf((T, n_kv * 128), seed, 2), bf((T, n_kv * 128), seed, 3)
+
+
+def check_attention_out(got, ref, offs, n_q, name, tol=2e-2):
+    for s, (a, b) in enumerate(zip(offs[:-1], offs[1:])):
+        for j in range(n_q):
+            hs = slice(j * 128, (j + 1) * 128)
+            check_block(got[a:b, hs], ref[a:b, hs], tol, "%s[seq %d, head %d]" % (name, s, j))
+
+
+@pytest.mark.parametrize("offs,n_q,n_kv", [([0, 1, 65, 200, 333], 8, 2), ([0, 1024, 2048], 32, 8),
+                                          ([0, 64, 64, 127, 128], 4, 1)])
+def test_attention_fwd(P, offs, n_q, n_kv):
+    import torch
+    log("attention fwd offs=%s n_q=%d n_kv=%d" % (offs, n_q, n_kv))
+    T = offs[-1]
+    q, k, v = attn_inputs(offs, n_q, n_kv, 65)
+    o = torch.full((T, n_q * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((n_q, T), float("nan"), dtype=torch.float32, device="cuda")
+    P.plora_attention_fwd(dev(q), dev(k), dev(v), o, lse, offs, n_q, n_kv)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = OB.attention_fwd(q, k, v, offs, n_q, n_kv)
+    check_attention_out(host(o), o_ref, offs, n_q, "o")
+    np.testing.assert_allclose(host(lse), lse_ref, rtol=1e-5, atol=1e-4)
