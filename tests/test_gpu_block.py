@@ -121,11 +121,15 @@ def attn_inputs(offs, n_q, n_kv, seed):
     return bf((T, n_q * 128), seed, 1), bf((T, n_kv * 128), seed, 2), bf((T, n_kv * 128), seed, 3)
 
 
-def check_attention_out(got, ref, offs, n_q, name, tol=2e-2):
+def check_attention_out(got, ref, offs, n_q, name, tol=2e-2, elementwise=True):
+    # blocks whose exact value vanishes (a one-token sequence's dQ) are measured
+    # against 1e-3 of the whole output's rms
+    floor = 1e-3 * float(np.sqrt(np.mean(np.square(ref))))
     for s, (a, b) in enumerate(zip(offs[:-1], offs[1:])):
         for j in range(n_q):
             hs = slice(j * 128, (j + 1) * 128)
-            check_block(got[a:b, hs], ref[a:b, hs], tol, "%s[seq %d, head %d]" % (name, s, j))
+            check_block(got[a:b, hs], ref[a:b, hs], tol, "%s[seq %d, head %d]" % (name, s, j), floor_rms=floor,
+                        elementwise=elementwise)
 
 
 @pytest.mark.parametrize("offs,n_q,n_kv", [([0, 1, 65, 200, 333], 8, 2), ([0, 1024, 2048], 32, 8),
@@ -142,3 +146,55 @@ def test_attention_fwd(P, offs, n_q, n_kv):
     o_ref, lse_ref = OB.attention_fwd(q, k, v, offs, n_q, n_kv)
     check_attention_out(host(o), o_ref, offs, n_q, "o")
     np.testing.assert_allclose(host(lse), lse_ref, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("offs,n_q,n_kv", [([0, 1, 65, 200, 333], 8, 2), ([0, 1024, 2048], 32, 8),
+                                          ([0, 100, 230], 16, 2), ([0, 64, 64, 127, 128], 4, 1)])
+def test_attention_bwd(P, offs, n_q, n_kv):
+    import torch
+    log("attention bwd offs=%s n_q=%d n_kv=%d" % (offs, n_q, n_kv))
+    T = offs[-1]
+    q, k, v = attn_inputs(offs, n_q, n_kv, 66)
+    dO = bf((T, n_q * 128), 66, 4)
+    o_ref, lse_ref = OB.attention_fwd(q, k, v, offs, n_q, n_kv)
+    o16 = rnd(o_ref)                          # the forward's stored output
+    lse32 = lse_ref.astype(np.float32)        # and its fp32 statistics
+    outs = [torch.full((T, n * 128), float("nan"), dtype=torch.bfloat16, device="cuda") for n in (n_q, n_kv, n_kv)]
+    delta = torch.full((n_q, T), float("nan"), dtype=torch.float32, device="cuda")
+    P.plora_attention_bwd(dev(q), dev(k), dev(v), dev(o16), dev32(lse32), dev(dO), *outs, delta, offs, n_q, n_kv)
+    torch.cuda.synchronize()
+    refs = OB.attention_bwd(dO, q, k, v, o16, lse32.astype(np.float64), offs, n_q, n_kv)
+    bounds = bwd_rounding_bounds(q, k, v, dO, o16, lse32.astype(np.float64), offs, n_q, n_kv)
+    for name, got, ref, nh, bd in zip(("dq", "dk", "dv"), outs, refs, (n_q, n_kv, n_kv), bounds):
+        got = host(got)
+        # Frobenius per block as for every kernel ...
+        check_attention_out(got, ref, offs, nh, name, elementwise=False)
+        # ... and elementwise against the rounding model: the kernel feeds P and dS
+        # to the matrix cores as bf16 (relative 2^-9 each), so an element may be
+        # off by 2^-9 * sum |dS| |K| (dq), sum |dS| |Q| (dk), sum P |dO| (dv),
+        # plus its own bf16 rounding; twice that is allowed
+        err = np.abs(got - ref)
+        lim = 2.0 * (bd + 2.0 ** -9 * np.abs(ref)) + 1e-6
+        assert np.all(err <= lim), "%s: %d elements beyond the rounding bound; worst ratio %.2f" % (
+            name, int(np.sum(err > lim)), float(np.max(err / lim)))
+
+
+def bwd_rounding_bounds(q, k, v, dO, o, lse, offs, n_q, n_kv):
+    """Per-element size of the bf16 rounding of P and dS in the backward
+    products: 2^-9 * (|dS| @ |K|, |dS|^T @ |Q|, P^T @ |dO|), in fp64."""
+    scale, grp = 1.0 / np.sqrt(128.0), n_q // n_kv
+    bq, bk, bv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for a, b in zip(offs[:-1], offs[1:]):
+        if b == a:
+            continue
+        mask = np.tril(np.ones((b - a, b - a), bool))
+        for j in range(n_q):
+            hs, gs = slice(j * 128, (j + 1) * 128), slice((j // grp) * 128, (j // grp + 1) * 128)
+            Q, K, V = (x.astype(np.float64) for x in (q[a:b, hs], k[a:b, gs], v[a:b, gs]))
+            dOh, Oh = dO[a:b, hs].astype(np.float64), o[a:b, hs].astype(np.float64)
+            Pm = np.where(mask, np.exp(Q @ K.T * scale - lse[j, a:b][:, None]), 0.0)
+            dS = Pm * (dOh @ V.T - np.sum(dOh * Oh, axis=1, keepdims=True))
+            bq[a:b, hs] += 2.0 ** -9 * scale * np.abs(dS) @ np.abs(K)
+            bk[a:b, gs] += 2.0 ** -9 * scale * np.abs(dS).T @ np.abs(Q)
+            bv[a:b, gs] += 2.0 ** -9 * Pm.T @ np.abs(dOh)
+    return bq, bk, bv
