@@ -26,12 +26,14 @@ Each backward function below is derived by hand from its forward (chain rule,
 no automatic differentiation); ``tests/test_oracle_block.py`` pins them to
 PyTorch autograd in float64, finite differences and closed forms.
 
-Storage points.  The GPU keeps activations in bf16 between kernels.  The block
-oracle (``block_forward`` / ``block_backward``) takes a ``store`` function
-applied wherever a kernel writes an activation, so that it can either keep
-fp64 throughout (store = identity) or round where the GPU rounds (store =
-round to bf16), which makes each step's comparison independent of earlier
-roundings.  The per-kernel functions take and return fp64 arrays.
+Storage points.  The GPU keeps activations in bf16 between kernels (the LoRA
+activations H, G and the per-row statistics in fp32).  The block oracle
+(``block_forward`` / ``block_backward``) takes a ``store`` function applied
+wherever a kernel writes a bf16 activation, so that it can either keep fp64
+throughout (store = identity) or round where the GPU rounds (store = round to
+bf16).  The projections are the packed LoRA operator's own oracle
+(``oracle.packed_lora``).  The per-kernel functions take and return fp64
+arrays.
 """
 from __future__ import annotations
 
@@ -178,3 +180,82 @@ def swiglu_bwd(da, g, u):
     da, g, u = (np.asarray(a, np.float64) for a in (da, g, u))
     sg = _sigmoid(g)
     return da * u * sg * (1.0 + g * (1.0 - sg)), da * g * sg
+
+
+# ---------------------------------------------------------------- the block
+PROJ = ("q", "k", "v", "o", "g", "u", "d")
+
+
+def proj_dims(hidden, n_q, n_kv, mlp, head=HEAD):
+    """(d_in, d_out) of every packed projection."""
+    return {"q": (hidden, n_q * head), "k": (hidden, n_kv * head), "v": (hidden, n_kv * head),
+            "o": (n_q * head, hidden), "g": (hidden, mlp), "u": (hidden, mlp), "d": (mlp, hidden)}
+
+
+def _proj(p, name, seg, want, **kw):
+    from . import packed_lora
+    d_in, d_out = p["dims"][name]
+    return packed_lora(seg, p["ranks"], p["alphas"], d_in, d_out, W=p["W"][name], A=p["A"][name], B=p["B"][name],
+                       want=want, **kw)
+
+
+def store32(a):
+    """What an fp32 buffer holds."""
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+def block_forward(p, x, seg, seq, store=identity, eps=RMS_EPS, store_f32=store32):
+    """Forward of the block; returns (out, cache).  p: dict with "w1", "w2"
+    (norm weights), "W", "A", "B" (per projection: frozen weight [d_out, d_in],
+    packed A [R, d_in], packed B [R, d_out]), "ranks", "alphas", "dims",
+    "n_q", "n_kv".  seg: adapter segment offsets; seq: sequence offsets.
+    store_f32 is applied where the GPU keeps fp32 (H, rstd, lse)."""
+    c = {"x": np.asarray(x, np.float64)}
+    h1, r1 = rmsnorm_fwd(x, p["w1"], eps)
+    c["h1"], c["r1"] = store(h1), store_f32(r1)
+    for n in ("q", "k", "v"):
+        r = _proj(p, n, seg, ("Y", "H"), X=c["h1"])
+        c[n], c["H" + n] = store(r["Y"]), store_f32(r["H"])
+    pos = positions_of(seq)
+    c["qr"], c["kr"] = store(rope_fwd(c["q"], pos)), store(rope_fwd(c["k"], pos))
+    att, lse = attention_fwd(c["qr"], c["kr"], c["v"], seq, p["n_q"], p["n_kv"])
+    c["att"], c["lse"] = store(att), store_f32(lse)
+    r = _proj(p, "o", seg, ("Y", "H"), X=c["att"])
+    c["o"], c["Ho"] = store(r["Y"]), store_f32(r["H"])
+    c["x2"] = store(c["x"] + c["o"])
+    h2, r2 = rmsnorm_fwd(c["x2"], p["w2"], eps)
+    c["h2"], c["r2"] = store(h2), store_f32(r2)
+    for n in ("g", "u"):
+        r = _proj(p, n, seg, ("Y", "H"), X=c["h2"])
+        c[n], c["H" + n] = store(r["Y"]), store_f32(r["H"])
+    c["a"] = store(swiglu_fwd(c["g"], c["u"]))
+    r = _proj(p, "d", seg, ("Y", "H"), X=c["a"])
+    c["dd_out"], c["Hd"] = store(r["Y"]), store_f32(r["H"])
+    out = store(c["x2"] + c["dd_out"])
+    return out, c
+
+
+def block_backward(p, c, dout, seg, seq, store=identity):
+    """Backward of the block from the forward's cache; returns (dx, grads)
+    with grads[name] = (dA, dB) for every projection (fp64)."""
+    dout = np.asarray(dout, np.float64)
+    grads = {}
+
+    def bwd(name, X, dY, H):
+        dX = store(_proj(p, name, seg, ("dX",), dY=dY)["dX"])
+        w = _proj(p, name, seg, ("dA", "dB"), X=X, dY=dY)  # the oracle recomputes H and G itself
+        grads[name] = (w["dA"], w["dB"])
+        return dX
+
+    da = bwd("d", c["a"], dout, c["Hd"])
+    dg, du = swiglu_bwd(da, c["g"], c["u"])
+    dg, du = store(dg), store(du)
+    dh2 = bwd("g", c["h2"], dg, c["Hg"]) + bwd("u", c["h2"], du, c["Hu"])
+    dx2 = store(dout + rmsnorm_bwd(dh2, c["x2"], p["w2"], c["r2"]))
+    datt = bwd("o", c["att"], dx2, c["Ho"])
+    dq, dk, dv = attention_bwd(datt, c["qr"], c["kr"], c["v"], c["att"], c["lse"], seq, p["n_q"], p["n_kv"])
+    pos = positions_of(seq)
+    dq, dk, dv = store(rope_bwd(store(dq), pos)), store(rope_bwd(store(dk), pos)), store(dv)
+    dh1 = bwd("q", c["h1"], dq, c["Hq"]) + bwd("k", c["h1"], dk, c["Hk"]) + bwd("v", c["h1"], dv, c["Hv"])
+    dx = store(dx2 + rmsnorm_bwd(dh1, c["x"], p["w1"], c["r1"]))
+    return dx, grads

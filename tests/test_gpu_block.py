@@ -198,3 +198,62 @@ def bwd_rounding_bounds(q, k, v, dO, o, lse, offs, n_q, n_kv):
             bk[a:b, gs] += 2.0 ** -9 * scale * np.abs(dS).T @ np.abs(Q)
             bv[a:b, gs] += 2.0 ** -9 * Pm.T @ np.abs(dOh)
     return bq, bk, bv
+
+
+def block_params(hidden, n_q, n_kv, mlp, ranks, seed):
+    import torch
+    from packed_adapter_lora_amd.block import proj_dims
+    dims = proj_dims(hidden, n_q, n_kv, mlp)
+    R = int(sum(ranks))
+    host_p = {"w1": 1.0 + bf((1, hidden), seed, 1, 0.1)[0], "w2": 1.0 + bf((1, hidden), seed, 2, 0.1)[0],
+              "W": {}, "A": {}, "B": {}, "dims": dims, "n_q": n_q, "n_kv": n_kv}
+    host_p["w1"], host_p["w2"] = rnd(host_p["w1"]), rnd(host_p["w2"])
+    for i, (n, (di, do)) in enumerate(sorted(dims.items())):
+        host_p["W"][n] = bf((do, di), seed, 10 + i, 1.0 / np.sqrt(di))
+        host_p["A"][n] = bf((R, di), seed, 20 + i, 0.25)
+        host_p["B"][n] = bf((R, do), seed, 30 + i, 0.1)
+    devp = {"w1": dev(host_p["w1"]), "w2": dev(host_p["w2"]),
+            "W": {n: dev(v) for n, v in host_p["W"].items()}, "A": {n: dev(v) for n, v in host_p["A"].items()},
+            "B": {n: dev(v) for n, v in host_p["B"].items()}}
+    return host_p, devp
+
+
+def test_decoder_block_fwd_bwd(P):
+    import torch
+    from packed_adapter_lora_amd.block import DecoderBlock, PROJ
+    hidden, n_q, n_kv, mlp = 512, 4, 1, 384
+    ranks, alphas = [8, 16, 4], [16.0, 16.0, 8.0]
+    seg, seq = [0, 150, 150, 256], [0, 100, 150, 256]
+    T = seg[-1]
+    log("decoder block T=%d hidden=%d heads=%d/%d mlp=%d" % (T, hidden, n_q, n_kv, mlp))
+    hp, dp = block_params(hidden, n_q, n_kv, mlp, ranks, 67)
+    x, dout = bf((T, hidden), 67, 90), bf((T, hidden), 67, 91)
+    blk = DecoderBlock(dp, seg, ranks, alphas, seq, hidden=hidden, n_q=n_q, n_kv=n_kv, mlp=mlp)
+    out = blk.forward(dev(x))
+    dx, grads = blk.backward(dev(dout))
+    torch.cuda.synchronize()
+    hp["ranks"], hp["alphas"] = np.array(ranks), np.array(alphas)
+    ref_out, cache = OB.block_forward(hp, x, seg, seq, store=rnd)
+    ref_dx, ref_grads = OB.block_backward(hp, cache, dout, seg, seq, store=rnd)
+    # This test checks the wiring of a chain of ~10 (forward) and ~25
+    # (backward) kernels, each verified alone above.  Each rounds to bf16; the
+    # oracle rounds at the same points, but a one-ulp difference at one step
+    # propagates, so tails of the elementwise error reach ~10 % of the rms
+    # while the Frobenius error stays below 1 %.  Held to: Frobenius 2e-2 and
+    # elementwise 2e-2 |ref| + 0.15 rms(ref); a wiring mistake (wrong buffer,
+    # order or fusion) is off by O(1).
+    def chain(got, ref, name):
+        got, ref = host(got), np.asarray(ref, np.float64)
+        check_block(got, ref, 2e-2, name, elementwise=False)
+        rms = float(np.sqrt(np.mean(ref * ref)))
+        err = np.abs(got - ref)
+        lim = 2e-2 * np.abs(ref) + 0.15 * rms
+        log("%s: rel Frobenius %.2e, worst elementwise %.2f of the bound" % (
+            name, np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30), float(np.max(err / lim))))
+        assert np.all(err <= lim), "%s: %d elements beyond the chained-rounding bound" % (name, int(np.sum(err > lim)))
+
+    chain(out, ref_out, "out")
+    chain(dx, ref_dx, "dx")
+    for n in PROJ:
+        chain(grads[n][0], ref_grads[n][0], "dA[%s]" % n)
+        chain(grads[n][1], ref_grads[n][1], "dB[%s]" % n)

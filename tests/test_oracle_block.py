@@ -187,3 +187,72 @@ def test_block_pins_catch_planted_mistakes(name, tmp_path):
         except (AssertionError, ValueError, IndexError, RuntimeError):
             failed += 1
     assert failed > 0, "planted mistake %s passed every pin" % name
+
+
+# ---------------------------------------------------------------- the composed block
+def small_block(seed=9, hidden=512, n_q=4, n_kv=1, mlp=96, ranks=(4, 8, 2), alphas=(8.0, 8.0, 4.0)):
+    rng = np.random.default_rng(seed)
+    dims = OB.proj_dims(hidden, n_q, n_kv, mlp)
+    R = sum(ranks)
+    p = {"w1": 1 + 0.1 * rng.standard_normal(hidden), "w2": 1 + 0.1 * rng.standard_normal(hidden),
+         "W": {}, "A": {}, "B": {}, "ranks": np.array(ranks), "alphas": np.array(alphas), "dims": dims,
+         "n_q": n_q, "n_kv": n_kv}
+    for n, (di, do) in dims.items():
+        p["W"][n] = rng.standard_normal((do, di)) / np.sqrt(di)
+        p["A"][n] = rng.standard_normal((R, di)) / np.sqrt(4)
+        p["B"][n] = rng.standard_normal((R, do)) * 0.2
+    return p
+
+
+def torch_block(p, x, seg, seq):
+    """The same block written with PyTorch float64 ops (rms_norm, SDPA, silu,
+    plain matrix products per adapter segment) for autograd."""
+    n_q, n_kv = p["n_q"], p["n_kv"]
+    W = {n: t64(p["W"][n]) for n in OB.PROJ}
+    A = {n: t64(p["A"][n], True) for n in OB.PROJ}
+    B = {n: t64(p["B"][n], True) for n in OB.PROJ}
+
+    def proj(n, X):
+        Y = X @ W[n].T
+        parts, ro = [], 0
+        for i, r in enumerate(p["ranks"]):
+            a, b = seg[i], seg[i + 1]
+            s = float(p["alphas"][i]) / r
+            parts.append(Y[a:b] + s * (X[a:b] @ A[n][ro:ro + r].T) @ B[n][ro:ro + r])
+            ro += r
+        return torch.cat(parts, 0)
+
+    def rope(t):
+        T = t.shape[0]
+        pos = torch.tensor(OB.positions_of(seq), dtype=torch.float64)
+        inv = 500000.0 ** (-torch.arange(0, 128, 2, dtype=torch.float64) / 128)
+        ang = (pos[:, None] * inv[None, :])[:, None, :]
+        th = t.reshape(T, -1, 128)
+        lo, hi = th[..., :64], th[..., 64:]
+        return torch.cat([lo * torch.cos(ang) - hi * torch.sin(ang), hi * torch.cos(ang) + lo * torch.sin(ang)],
+                         -1).reshape(T, -1)
+
+    xt = t64(x, True)
+    h1 = F.rms_norm(xt, (xt.shape[1],), t64(p["w1"]), eps=1e-5)
+    q, k, v = rope(proj("q", h1)), rope(proj("k", h1)), proj("v", h1)
+    att = _sdpa(q, k, v, seq, n_q, n_kv, 128)
+    x2 = xt + proj("o", att)
+    h2 = F.rms_norm(x2, (x2.shape[1],), t64(p["w2"]), eps=1e-5)
+    out = x2 + proj("d", F.silu(proj("g", h2)) * proj("u", h2))
+    return out, xt, A, B
+
+
+def test_block_oracle_matches_torch_autograd():
+    p = small_block()
+    seg, seq = [0, 40, 40, 70], [0, 25, 40, 70]
+    rng = np.random.default_rng(10)
+    x, dout = rng.standard_normal((70, 512)), rng.standard_normal((70, 512))
+    out, cache = OB.block_forward(p, x, seg, seq, store_f32=OB.identity)  # fp64 throughout
+    ot, xt, At, Bt = torch_block(p, x, seg, seq)
+    np.testing.assert_allclose(out, ot.detach().numpy(), rtol=1e-10, atol=1e-10)
+    ot.backward(t64(dout))
+    dx, grads = OB.block_backward(p, cache, dout, seg, seq)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    for n in OB.PROJ:
+        np.testing.assert_allclose(grads[n][0], At[n].grad.numpy(), rtol=1e-9, atol=1e-10, err_msg="dA " + n)
+        np.testing.assert_allclose(grads[n][1], Bt[n].grad.numpy(), rtol=1e-9, atol=1e-10, err_msg="dB " + n)
