@@ -324,6 +324,118 @@ def cpu_baseline(wl, inp, per_segment):
                       "G, dA, dB over them; %.1f s" % (per_segment, wl.n_adapters, len(rows), dt)}
 
 
+BLOCK_DIMS = {"hidden": 4096, "n_q": 32, "n_kv": 8, "mlp": 14336}
+
+
+def block_setup(n_adapters, tokens_each, seed=5):
+    """The Llama-3-8B decoder-block workload: N adapters x tokens_each tokens
+    (one sequence per adapter), ranks cycling 8/16/32/64, alphas 8/16/32, LoRA
+    on all seven projections; seeded synthetic weights and activations."""
+    import workloads
+    ranks = [[8, 16, 32, 64][i % 4] for i in range(n_adapters)]
+    alphas = [[8.0, 16.0, 32.0][i % 3] for i in range(n_adapters)]
+    seg = np.arange(n_adapters + 1, dtype=np.int64) * tokens_each
+    from packed_adapter_lora_amd.block import proj_dims
+    dims = proj_dims(**BLOCK_DIMS)
+    R = sum(ranks)
+    hp = {"w1": 1.0 + workloads.draw(seed, 101, (1, BLOCK_DIMS["hidden"]), 0.1, "bf16")[0],
+          "w2": 1.0 + workloads.draw(seed, 102, (1, BLOCK_DIMS["hidden"]), 0.1, "bf16")[0], "W": {}, "A": {}, "B": {},
+          "ranks": np.array(ranks), "alphas": np.array(alphas), "dims": dims, "n_q": BLOCK_DIMS["n_q"],
+          "n_kv": BLOCK_DIMS["n_kv"]}
+    for w in ("w1", "w2"):
+        hp[w] = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(hp[w]))
+    for i, (n, (di, do)) in enumerate(sorted(dims.items())):
+        hp["W"][n] = workloads.draw(seed, 110 + i, (do, di), 1.0 / np.sqrt(di), "bf16")
+        hp["A"][n] = workloads.draw(seed, 120 + i, (R, di), 0.1, "bf16")
+        hp["B"][n] = workloads.draw(seed, 130 + i, (R, do), float(np.sqrt(0.02)), "bf16")
+    T = int(seg[-1])
+    x = workloads.draw(seed, 140, (T, BLOCK_DIMS["hidden"]), 1.0, "bf16")
+    dout = workloads.draw(seed, 141, (T, BLOCK_DIMS["hidden"]), 1.0, "bf16")
+    return hp, seg, ranks, alphas, x, dout
+
+
+def block_flops(seg, ranks, hp):
+    """Algorithmic FLOPs of one block step: per projection 4 T d_in d_out + 6 sum n_i r_i (d_in + d_out);
+    attention 2 (forward) + 5 (backward) products of 2 * 128 * n_q * sum_s n_s (n_s + 1) / 2."""
+    counts = np.diff(seg)
+    nr = float(np.sum(counts * np.asarray(ranks)))
+    T = float(seg[-1])
+    f = sum(4.0 * T * di * do + 6.0 * nr * (di + do) for di, do in hp["dims"].values())
+    pairs = float(np.sum(counts * (counts + 1) / 2.0))
+    return f + 7 * 2.0 * 128 * hp["n_q"] * pairs
+
+
+def run_block_bench(args):
+    import torch
+    import packed_adapter_lora_amd as P
+    from packed_adapter_lora_amd.block import DecoderBlock
+    n, te = args.adapters or 32, 1024
+    log("decoder block: %d adapters x %d tokens, Llama-3-8B dims %s" % (n, te, BLOCK_DIMS))
+    hp, seg, ranks, alphas, x, dout = block_setup(n, te)
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    dp = {"w1": tb(hp["w1"]), "w2": tb(hp["w2"]), "W": {k: tb(v) for k, v in hp["W"].items()},
+          "A": {k: tb(v) for k, v in hp["A"].items()}, "B": {k: tb(v) for k, v in hp["B"].items()}}
+    blk = DecoderBlock(dp, seg, ranks, alphas, seg, **BLOCK_DIMS)
+    xd, dd = tb(x), tb(dout)
+
+    def step():
+        blk.forward(xd)
+        blk.backward(dd)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    P.plora_profile_reset()
+    P.plora_profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    P.plora_profile_enable(False)
+    kern = {}
+    for cls in ("gemm_fwd", "gemm_bwd", "shrink", "wgrad", "reduce", "norm", "rope", "swiglu", "add", "attn_fwd",
+                "attn_bwd"):
+        cnt, ms = P.plora_profile_read(cls)
+        if cnt:
+            kern[cls] = round(ms / args.steps, 4)
+    P.plora_profile_reset()
+    T = int(seg[-1])
+    flops = block_flops(seg, ranks, hp)
+    achieved = flops / sec / 1e12
+    out = {"metric": "decoder block fwd+bwd tokens/sec (LoRA on 7 projections, %d adapters)" % n,
+           "value": round(T / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic (seeded normal draws; no dataset or checkpoint)",
+           "config": {"workload": "llama3_8b_decoder_block_%d_adapters_x_%d_tokens" % (n, te), **BLOCK_DIMS,
+                      "tokens": T, "ranks": sorted(set(ranks)), "sequence": te},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": "whole block step",
+                        "flops_per_step": flops},
+           "kernels_ms_per_step": kern, "cpu_baseline": None}
+    if not args.no_cpu:
+        log("timing the oracle block on the host ...")
+        out["cpu_baseline"] = block_cpu_baseline(hp, seg, ranks, alphas, x, dout, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def block_cpu_baseline(hp, seg, ranks, alphas, x, dout, per_segment):
+    """fp64 oracle block (forward + backward) on the first `per_segment` tokens
+    of the first two adapters' sequences (a bounded sample)."""
+    import oracle
+    from oracle import block as OB
+    rows = np.concatenate([np.arange(seg[i], seg[i] + per_segment) for i in range(2)])
+    sub = np.array([0, per_segment, 2 * per_segment] + [2 * per_segment] * (len(ranks) - 2), dtype=np.int64)
+    p = dict(hp)
+    t0 = time.perf_counter()
+    out, c = OB.block_forward(p, x[rows], sub, np.array([0, per_segment, 2 * per_segment], np.int64))
+    OB.block_backward(p, c, dout[rows], sub, np.array([0, per_segment, 2 * per_segment], np.int64))
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "first %d tokens of the first 2 adapters' sequences (%d tokens), full Llama-3-8B block dims, "
+                      "forward and backward with all 7 projections' dA/dB; %.1f s" % (per_segment, len(rows), dt)}
+
+
 def write_profiles(d, workload):
     import workloads
     wl = workloads.config(workload)
@@ -362,6 +474,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample: tokens per segment")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--block", action="store_true",
+                    help="time the Llama-3-8B decoder block (LoRA on all 7 projections) instead of the operator")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--rocprof-summary", default=None,
@@ -370,6 +484,12 @@ def main():
     args = ap.parse_args()
     if args.rocprof_summary:
         write_profiles(args.rocprof_summary, args.workload)
+        return
+    if args.block:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only (--gpus %d requested)" % args.gpus, file=sys.stderr)
+            sys.exit(2)
+        run_block_bench(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the packed-LoRA operator here has no multi-GPU path "
