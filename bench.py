@@ -436,6 +436,25 @@ def block_cpu_baseline(hp, seg, ranks, alphas, x, dout, per_segment):
                       "forward and backward with all 7 projections' dA/dB; %.1f s" % (per_segment, len(rows), dt)}
 
 
+def write_block_profile(d):
+    """Kernel-time summary of a rocprofv3 --kernel-trace --stats run of the block bench."""
+    import csv
+    import glob
+    cmds = json.load(open(os.path.join(d, "commands.json")))
+    f = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    rows = list(csv.DictReader(open(f[0])))
+    lines = ["# rocprofv3 kernel statistics, Llama-3-8B decoder block, 32 adapters x 1024 tokens",
+             "# command: " + cmds["trace"], "",
+             "%6s %12s %12s %7s  %s" % ("calls", "total_ms", "avg_us", "pct", "kernel")]
+    for r in rows:
+        lines.append("%6s %12.3f %12.1f %7.2f  %s" % (r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+                                                      float(r["AverageNs"]) / 1e3, float(r["Percentage"]),
+                                                      r["Name"][:110]))
+    txt = "\n".join(lines) + "\n"
+    open(os.path.join(ROOT, "profiles", "kernels_llama3_8b_block_stats.txt"), "w").write(txt)
+    print(txt)
+
+
 def write_profiles(d, workload):
     import workloads
     wl = workloads.config(workload)
@@ -483,7 +502,10 @@ def main():
                          "write summaries under profiles/ and exit")
     args = ap.parse_args()
     if args.rocprof_summary:
-        write_profiles(args.rocprof_summary, args.workload)
+        if args.block:
+            write_block_profile(args.rocprof_summary)
+        else:
+            write_profiles(args.rocprof_summary, args.workload)
         return
     if args.block:
         if args.gpus != 1:
