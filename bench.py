@@ -354,6 +354,54 @@ def block_setup(n_adapters, tokens_each, seed=5):
     return hp, seg, ranks, alphas, x, dout
 
 
+def decode_bytes(wl):
+    """Algorithmic HBM bytes of one decode-shaped forward: W, the packed A and
+    B panels, X, Y and H written and read once (bf16 operands, fp32 H)."""
+    nr = float(np.sum(np.diff(wl.offsets) * wl.ranks))
+    return 2.0 * (wl.d_in * wl.d_out + wl.R * (wl.d_in + wl.d_out) + wl.T * (wl.d_in + wl.d_out)) + 8.0 * nr
+
+
+def run_decode_bench(args):
+    """Forward-only multi-LoRA at serving shapes (1 to 16 tokens per adapter):
+    latency of plora_forward, bound by HBM (the frozen W and the adapters'
+    panels are each read once)."""
+    import torch
+    import packed_adapter_lora_amd as P
+    import workloads
+    name = args.workload if args.workload.startswith("decode") else "decode_up"
+    wl = workloads.config(name, n_adapters=args.adapters)
+    log("decode workload %s: T=%d d_in=%d d_out=%d N=%d R=%d" % (wl.name, wl.T, wl.d_in, wl.d_out, wl.n_adapters,
+                                                                  wl.R))
+    inp = workloads.make_inputs(wl, which=("W", "A", "B", "X"))
+    dev = {k: torch.from_numpy(v).to("cuda").to(torch.bfloat16) for k, v in inp.items()}
+    d = P.Desc.from_workload(wl)
+    Y = torch.empty((wl.T, wl.d_out), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((P.plora_h_elems(d),), dtype=torch.float32, device="cuda")
+    calls = max(args.steps, 20) * 5
+    for _ in range(args.warmup * 5):
+        P.plora_forward(d, dev["X"], dev["W"], dev["A"], dev["B"], Y, H)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        P.plora_forward(d, dev["X"], dev["W"], dev["A"], dev["B"], Y, H)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    nbytes = decode_bytes(wl)
+    out = {"metric": "decode-shaped packed LoRA forward latency (%d adapters, %d tokens)" % (wl.n_adapters, wl.T),
+           "value": round(us, 2), "unit": "us", "n_gpus": 1, "steps": calls, "warmup": args.warmup * 5,
+           "higher_is_better": False, "dtype": "bf16", "data": "synthetic (seeded normal draws)",
+           "config": {"workload": wl.name, "d_in": wl.d_in, "d_out": wl.d_out, "n_adapters": wl.n_adapters,
+                      "tokens": wl.T, "tokens_per_adapter": sorted(set(np.diff(wl.offsets).tolist())),
+                      "sum_ranks": wl.R},
+           "tokens_per_s": round(wl.T / (us * 1e-6), 1),
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "bytes_per_call": nbytes}}
+    print(json.dumps(out), flush=True)
+
+
 def block_flops(seg, ranks, hp):
     """Algorithmic FLOPs of one block step: per projection 4 T d_in d_out + 6 sum n_i r_i (d_in + d_out);
     attention 2 (forward) + 5 (backward) products of 2 * 128 * n_q * sum_s n_s (n_s + 1) / 2."""
@@ -493,6 +541,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample: tokens per segment")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the forward at decode shapes (--workload decode_up or decode_sq)")
     ap.add_argument("--block", action="store_true",
                     help="time the Llama-3-8B decoder block (LoRA on all 7 projections) instead of the operator")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -506,6 +556,12 @@ def main():
             write_block_profile(args.rocprof_summary)
         else:
             write_profiles(args.rocprof_summary, args.workload)
+        return
+    if args.decode:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only (--gpus %d requested)" % args.gpus, file=sys.stderr)
+            sys.exit(2)
+        run_decode_bench(args)
         return
     if args.block:
         if args.gpus != 1:

@@ -154,24 +154,38 @@ __device__ __forceinline__ void lora_expand(f32x16 (&acc)[4][4], const GemmArgs&
                 *reinterpret_cast<u16x8*>(slo + kmaj(tid, c)) = lo;
             }
             __syncthreads();
-            for (int kk = 0; kk < nkk; ++kk) {
+            // only this wave's 32-token blocks that hold tokens of the segment
+            // have nonzero F rows: the others skip their MFMAs (many adapters
+            // with few tokens each share a tile at serving shapes)
+            bool live[4];
+            bool any = false;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int64_t b0 = q0 + wq * 128 + nt * 32;
+                live[nt] = b0 < s1 && b0 + 32 > s0;
+                any |= live[nt];
+            }
+            for (int kk = 0; any && kk < nkk; ++kk) {
                 bf16x8 fa[4], fh[4], fl[4];
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     fa[mt] = pfrag_rows(se, se_row, wp * 128 + mt * 32 + l32, 16 * kk + 8 * lh);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
+                    if (!live[nt]) continue;
                     const int row = wq * 128 + nt * 32 + l32;
                     fh[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(shi + kmaj(row, 2 * kk + lh)));
                     fl[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(slo + kmaj(row, 2 * kk + lh)));
                 }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int nt = 0; nt < 4; ++nt) {
+                    if (!live[nt]) continue;
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
+                    for (int mt = 0; mt < 4; ++mt) {
                         acc[mt][nt] = mfma32x32x16(fa[mt], fh[nt], acc[mt][nt]);
                         acc[mt][nt] = mfma32x32x16(fa[mt], fl[nt], acc[mt][nt]);
                     }
+                }
             }
         }
     }

@@ -280,3 +280,11 @@ def test_llama_sq_2_adapters(P):
 @pytest.mark.parametrize("proj", ["k", "down"])
 def test_block_projection(P, proj):
     sampled_case(P, workloads.config("block_" + proj, n_adapters=8), per_segment=2)
+
+
+@pytest.mark.parametrize("name", ["decode_sq", "decode_up"])
+def test_decode_shapes_full(P, name):
+    """Serving shapes: 64 adapters with 1 to 16 tokens each (many adapters
+    per token tile), compared in full (forward only is what serving runs; the
+    backward is covered too)."""
+    full_case(P, workloads.config(name))

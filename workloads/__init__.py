@@ -112,6 +112,10 @@ def config(name: str, n_adapters: int | None = None, tokens_each: int | None = N
     longtail  4096->14336 bf16, 16 adapters, lognormal token counts
     block_<p> one Llama-3-8B decoder projection p in q,k,v,o,gate,up,down,
               32 adapters x 1024 tokens
+    decode_up, decode_sq
+              decode-shaped serving batches on the llama_up / llama_sq
+              shapes: N adapters (default 64) with 1, 2, 4, 8, 16 tokens
+              (cycling; 397 tokens at N = 64), ranks cycle 8..64
     """
     if name == "tiny":
         return Workload("tiny", 256, 256, _offsets([64, 64]), np.array([4, 8], np.int32),
@@ -134,6 +138,13 @@ def config(name: str, n_adapters: int | None = None, tokens_each: int | None = N
         alphas = np.array([_ALPHA_CYCLE[i % 3] for i in range(16)], dtype=np.float32)
         return Workload("longtail", 4096, 14336, _offsets(counts), ranks.astype(np.int32), alphas,
                         "bf16", seed, w_var=1.0 / 4096)
+    if name in ("decode_up", "decode_sq"):
+        n = 64 if n_adapters is None else n_adapters
+        d_out = 14336 if name == "decode_up" else 4096
+        counts = [[1, 2, 4, 8, 16][i % 5] for i in range(n)] if tokens_each is None else [tokens_each] * n
+        ranks = np.array([_RANK_CYCLE[i % 4] for i in range(n)], dtype=np.int32)
+        alphas = np.array([_ALPHA_CYCLE[i % 3] for i in range(n)], dtype=np.float32)
+        return Workload(name, 4096, d_out, _offsets(counts), ranks, alphas, "bf16", 6, w_var=1.0 / 4096)
     if name.startswith("block_"):
         proj = name[len("block_"):]
         shapes = {"q": (4096, 4096), "k": (4096, 1024), "v": (4096, 1024), "o": (4096, 4096),
