@@ -43,6 +43,14 @@ class plora_desc(ctypes.Structure):
     ]
 
 
+class plora_job(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("mem_bytes", ctypes.c_double), ("ms_per_step", ctypes.c_double)]
+
+
+class plora_pack_model(ctypes.Structure):
+    _fields_ = [("mem_budget", ctypes.c_double), ("fixed_ms", ctypes.c_double), ("mem_quantum", ctypes.c_double)]
+
+
 class plora_adamw_config(ctypes.Structure):
     _fields_ = [
         ("beta1", ctypes.c_float),
@@ -56,7 +64,7 @@ class plora_adamw_config(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libplora.so is not built (run: python -m packed_adapter_lora_amd.build)")
+        raise ImportError("libplora.so is not built (run: python packed_adapter_lora_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, dp = ctypes.c_void_p, ctypes.POINTER(plora_desc)
     fp = ctypes.c_void_p
@@ -77,6 +85,12 @@ def _load():
         "plora_add": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
         "plora_attention_fwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 6),
         "plora_attention_bwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 11),
+        "plora_plan_packs": (ctypes.c_int, [ctypes.POINTER(plora_job), ctypes.c_int32, ctypes.POINTER(plora_pack_model),
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_double)]),
+        "plora_plan_makespan": (ctypes.c_double, [ctypes.POINTER(plora_job), ctypes.c_int32,
+                                                  ctypes.POINTER(plora_pack_model), ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.c_int32]),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
         "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
         "plora_validate": (ctypes.c_int, [dp]),
@@ -371,3 +385,37 @@ def plora_attention_bwd(q, k, v, o, lse, dO, dq, dk, dv, delta, seq_offsets, n_q
     _check_tensor("delta", delta, (n_q, T), "float32")
     _check(_lib.plora_attention_bwd(n, p, n_q, n_kv, _addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dO),
                                     _addr(dq), _addr(dk), _addr(dv), _addr(delta), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Packing planner (include/plora_planner.h), host only.
+# ---------------------------------------------------------------------------
+
+def _jobs(steps, mem_bytes, ms_per_step):
+    n = len(steps)
+    arr = (plora_job * n)()
+    for k in range(n):
+        arr[k].steps, arr[k].mem_bytes, arr[k].ms_per_step = int(steps[k]), float(mem_bytes[k]), float(ms_per_step[k])
+    return arr, n
+
+
+def plora_plan_packs(steps, mem_bytes, ms_per_step, mem_budget, fixed_ms, mem_quantum):
+    """Returns (pack_of_job as an int32 array, n_packs, makespan_ms)."""
+    arr, n = _jobs(steps, mem_bytes, ms_per_step)
+    model = plora_pack_model(mem_budget, fixed_ms, mem_quantum)
+    out = np.empty(n, dtype=np.int32)
+    npk, ms = ctypes.c_int32(0), ctypes.c_double(0.0)
+    _check(_lib.plora_plan_packs(arr, n, ctypes.byref(model), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 ctypes.byref(npk), ctypes.byref(ms)))
+    return out, int(npk.value), float(ms.value)
+
+
+def plora_plan_makespan(steps, mem_bytes, ms_per_step, mem_budget, fixed_ms, mem_quantum, pack_of_job, n_packs):
+    arr, n = _jobs(steps, mem_bytes, ms_per_step)
+    model = plora_pack_model(mem_budget, fixed_ms, mem_quantum)
+    p = np.ascontiguousarray(pack_of_job, dtype=np.int32)
+    v = _lib.plora_plan_makespan(arr, n, ctypes.byref(model), p.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 int(n_packs))
+    if v < 0:
+        _check(int(v))
+    return float(v)

@@ -1,6 +1,6 @@
 """Build libplora.so in-tree for gfx950 (hipcc) -- no JIT, no torch extension.
 
-    python -m packed_adapter_lora_amd.build
+    python packed_adapter_lora_amd/build.py
 
 Every HIP source is compiled with packed-fp32 instructions disabled (the
 compiler otherwise forms v_pk_* fp32 ops from ordinary float code).
@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "api_block.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip", "optim.hip",
                "block.hip", "attention.hip"]
-CXX_SOURCES = ["plan.cpp"]
+CXX_SOURCES = ["plan.cpp", "planner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
