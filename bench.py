@@ -467,6 +467,87 @@ def run_block_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def time_block_step(n_adapters, tokens_each, steps=3, warmup=1):
+    """Seconds per forward+backward step of one decoder block."""
+    import torch
+    from packed_adapter_lora_amd.block import DecoderBlock
+    hp, seg, ranks, alphas, x, dout = block_setup(n_adapters, tokens_each)
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda").to(torch.bfloat16)
+    dp = {"w1": tb(hp["w1"]), "w2": tb(hp["w2"]), "W": {k: tb(v) for k, v in hp["W"].items()},
+          "A": {k: tb(v) for k, v in hp["A"].items()}, "B": {k: tb(v) for k, v in hp["B"].items()}}
+    blk = DecoderBlock(dp, seg, ranks, alphas, seg, **BLOCK_DIMS)
+    xd, dd = tb(x), tb(dout)
+    for _ in range(warmup):
+        blk.forward(xd)
+        blk.backward(dd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        blk.forward(xd)
+        blk.backward(dd)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def plan_jobs(n_jobs=120, layers=32, dataset=2000, epochs=3, seq=1024):
+    """The fine-tuning jobs of a hyper-parameter search like the pages' 120
+    configurations (rank, batch size, learning rate, scale varied): ranks
+    8..64, batch sizes 1..8 sequences of 1024 tokens, `epochs` passes over
+    `dataset` sequences.  Memory per job on Llama-3-8B (32 layers, LoRA on the
+    7 projections): 18 bytes per adapter parameter (fp32 master, two fp32
+    moments, fp32 gradient, bf16 copy) and the activations the backward keeps
+    (136 KiB per token per layer in bf16: x, h1, q, k, v, attention output, x2,
+    h2, gate, up, SwiGLU output)."""
+    from packed_adapter_lora_amd.block import proj_dims
+    dims = proj_dims(**BLOCK_DIMS)
+    per_rank = layers * sum(di + do for di, do in dims.values())
+    act_per_token = layers * 2.0 * (6 * 4096 + 2 * 1024 + 3 * 14336)
+    jobs = []
+    for k in range(n_jobs):
+        r = [8, 16, 32, 64][k % 4]
+        bs = [1, 2, 4, 8][(k // 4) % 4]
+        tokens = bs * seq
+        steps = epochs * dataset // bs
+        jobs.append({"rank": r, "tokens": tokens, "steps": steps, "mem": 18.0 * r * per_rank + act_per_token * tokens})
+    return jobs
+
+
+def run_plan_bench(args):
+    """Plan a 120-job LoRA search on one GPU with the cost model fitted on the
+    decoder block (two sizes), and compare the planned makespan with running
+    the jobs one at a time."""
+    import packed_adapter_lora_amd as P
+    layers = 32
+    log("fitting the step-time model on the decoder block (1024 and 32768 tokens) ...")
+    t_small = time_block_step(1, 1024)
+    t_big = time_block_step(32, 1024)
+    per_token = (t_big - t_small) / (32768 - 1024)   # seconds per token per layer
+    fixed = max(t_small - per_token * 1024, 0.0)      # seconds per step per layer
+    jobs = plan_jobs(layers=layers)
+    budget = 288e9 - 16.1e9 - 8e9   # HBM minus the bf16 base model and working buffers
+    steps = [j["steps"] for j in jobs]
+    mem = [j["mem"] for j in jobs]
+    own = [j["tokens"] * per_token * layers * 1e3 for j in jobs]  # ms per step
+    fixed_ms = fixed * layers * 1e3
+    t0 = time.perf_counter()
+    assign, npk, makespan = P.plora_plan_packs(steps, mem, own, budget, fixed_ms, 2 ** 26)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    seq_ms = sum(s * (fixed_ms + o) for s, o in zip(steps, own))
+    lower = fixed_ms * max(steps) + sum(s * o for s, o in zip(steps, own))
+    out = {"metric": "planned packing speedup over one job at a time (120 LoRA fine-tuning jobs, one MI355X)",
+           "value": round(seq_ms / makespan, 3), "unit": "x", "higher_is_better": True, "n_gpus": 1,
+           "data": "synthetic job set; cost model measured on the decoder block",
+           "config": {"workload": "llama3_8b_lora_search_120_jobs", "layers": layers, "ranks": [8, 16, 32, 64],
+                      "batch_sequences": [1, 2, 4, 8], "sequence": 1024, "memory_budget_GB": round(budget / 1e9, 1)},
+           "plan": {"packs": npk, "makespan_h": round(makespan / 3.6e6, 3),
+                    "one_at_a_time_h": round(seq_ms / 3.6e6, 3), "lower_bound_h": round(lower / 3.6e6, 3),
+                    "planner_ms": round(plan_ms, 2)},
+           "cost_model": {"fixed_ms_per_step_per_layer": round(fixed * 1e3, 4),
+                          "us_per_token_per_layer": round(per_token * 1e6, 5),
+                          "measured": "decoder block fwd+bwd at 1 x 1024 and 32 x 1024 tokens"}}
+    print(json.dumps(out), flush=True)
+
+
 def block_cpu_baseline(hp, seg, ranks, alphas, x, dout, per_segment):
     """fp64 oracle block (forward + backward) on the first `per_segment` tokens
     of the first two adapters' sequences (a bounded sample)."""
@@ -541,6 +622,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample: tokens per segment")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--plan", action="store_true",
+                    help="plan a 120-job LoRA search with the packing planner (cost model fitted on the GPU)")
     ap.add_argument("--decode", action="store_true",
                     help="time the forward at decode shapes (--workload decode_up or decode_sq)")
     ap.add_argument("--block", action="store_true",
@@ -556,6 +639,12 @@ def main():
             write_block_profile(args.rocprof_summary)
         else:
             write_profiles(args.rocprof_summary, args.workload)
+        return
+    if args.plan:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only (--gpus %d requested)" % args.gpus, file=sys.stderr)
+            sys.exit(2)
+        run_plan_bench(args)
         return
     if args.decode:
         if args.gpus != 1:

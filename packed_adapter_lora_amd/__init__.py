@@ -63,6 +63,14 @@ class plora_adamw_config(ctypes.Structure):
 
 
 def _load():
+    # Load PyTorch's HIP runtime first when PyTorch is installed: libplora.so
+    # then binds to that same runtime.  Loaded the other way round, the process
+    # would hold two HIP runtimes (the system one for this library, PyTorch's
+    # bundled one for the tensors) and this library's would find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError("libplora.so is not built (run: python packed_adapter_lora_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
