@@ -48,10 +48,22 @@ __device__ __forceinline__ u32x4 load16_or_zero(const void* p, bool pred) {
     return z;
 }
 
-// Adapter owning token t: the i with off[i] <= t < off[i+1] (N <= 64, linear).
+// Adapter owning token t: the last i with off[i] <= t, i.e. off[i] <= t <
+// off[i+1] with empty segments skipped (binary search: with uniform t the
+// table reads are a short chain of scalar loads).
 __device__ __forceinline__ int segment_of(const SegTable& s, int64_t t) {
-    int i = 0;
-    while (i + 1 < s.n && s.off[i + 1] <= t) ++i;
+    int lo = 0, hi = s.n;  // off[lo] <= t, and off[hi] > t or hi == n
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s.off[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// The same search restricted to adapters i0 .. i1 (i0's segment starts at or before t).
+__device__ __forceinline__ int segment_in(const SegTable& s, int i0, int i1, int64_t t) {
+    int i = i0;
+    while (i < i1 && s.off[i + 1] <= t) ++i;
     return i;
 }
 

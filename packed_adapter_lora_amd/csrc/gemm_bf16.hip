@@ -409,6 +409,194 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_w0[kPipeTile];  // weight ti
 __shared__ __attribute__((aligned(1024))) uint8_t g_w1[kPipeTile];
 
 
+// LoRA expand of the pipelined kernel.  The adapters whose segments overlap
+// the tile are expanded together, over their ranks laid out in a 16-aligned
+// rank space (adapter i owns virtual ranks voff[i] .. voff[i]+r_i-1, the rest
+// of its 16-rank groups is zero), in chunks of 64 virtual ranks, however many
+// adapters share the tile.  A 16-rank k-step therefore always holds ranks of
+// one adapter in the same grouping as when that adapter runs alone, so the
+// packed result equals the separate one bit for bit.  E rows of a chunk (p-
+// contiguous, 512 bytes) arrive by LDS DMA, double-buffered, read transposed;
+// F is block-diagonal: thread tid fills token row q0 + tid with s_i * H_i of
+// its own adapter where the chunk covers that adapter's ranks and zero
+// elsewhere (bf16 hi/lo).  The next chunk's loads are in flight during the
+// current chunk's MFMAs, and per 16-rank k-step only the 32-token blocks
+// holding tokens of the k-step's adapter multiply.  e0/e1 (E), shi/slo (F),
+// tab (virtual rank -> E row table, at most 8192 entries): 32 KiB each, free.
+__device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const GemmArgs& a, const SegTable& seg,
+                                                 int64_t q0, int64_t p0, uint8_t* e0, uint8_t* e1, uint8_t* shi,
+                                                 uint8_t* slo, uint8_t* tab) {
+    const int64_t T = a.T, Pdim = a.Pdim;
+    const int tid = (int)threadIdx.x, l = lane_id(), w = wave_id();
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+    const int64_t tlast = (q0 + kBQ < T ? q0 + kBQ : T) - 1;
+    const int i_first = segment_of(seg, q0), i_last = segment_in(seg, i_first, seg.n - 1, tlast);
+    const int vlo = seg.voff[i_first], vhi = seg.voff[i_last + 1];
+    const int nch = (vhi - vlo + 63) >> 6;
+    if (nch <= 0) return;
+
+    // E rows: buffer from column p0; row j at j * Pdim * 2 bytes; rows past R read zero
+    const int R = seg.roff[seg.n];
+    const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const bf16*>(a.E) + p0), 0, (int)(((int64_t)R * Pdim - p0) * 2), kRsrcWord3);
+    const int tr = l >> 5;
+    const uint32_t lane_t0 = (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
+    const uint32_t lane_t1 = (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
+    // virtual rank rows j0 .. j0+63 (those below vhi); wave: 1 KiB blocks 8w .. 8w+7 of 2
+    // rows v, v+1 (same adapter: adapters start at multiples of 16).  Padding rows read zero.
+    // Table: byte offset of the E row of virtual rank vlo + i (0x80000000 for padding: reads zero)
+    const int* rowtab = reinterpret_cast<const int*>(tab);
+    for (int i = i_first; i <= i_last; ++i) {
+        const int vb = seg.voff[i] - vlo, vn = seg.voff[i + 1] - seg.voff[i], r = seg.rank[i], rb = seg.roff[i];
+        for (int k = tid; k < vn; k += kThreads)
+            reinterpret_cast<int*>(tab)[vb + k] = k < r ? (int)((int64_t)(rb + k) * Pdim * 2) : (int)0x80000000u;
+    }
+    auto issue_e = [&](uint8_t* buf, int j0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int blk = 8 * wu + j;
+            const int v = j0 + 2 * blk;
+            if (v >= vhi) break;
+            const uint32_t vo = ((j & 1) ? lane_t1 : lane_t0) + (uint32_t)rowtab[v + tr - vlo];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
+        }
+    };
+
+    // this thread's token row: adapter, its virtual rank range, its H row and scale.
+    // The search runs over the tile's adapters with uniform indices (table reads
+    // stay scalar); each lane keeps the entry that holds its token.
+    const int64_t t = q0 + tid;
+    int va = 0, rt = 0;
+    float sc = 0.0f;
+    int64_t hbase = 0;
+    for (int i = i_first; i <= i_last; ++i) {
+        if (t >= seg.off[i] && t < seg.off[i + 1]) {
+            va = seg.voff[i];
+            rt = seg.rank[i];
+            sc = seg.scale[i];
+            hbase = seg.hoff[i] + (t - seg.off[i]) * seg.rank[i];
+        }
+    }
+    const float* hrow = a.F + hbase;
+    // 16-byte loads need every 4-rank group to be inside or outside the row
+    const bool vec = (hbase & 3) == 0 && (rt & 3) == 0;
+    float fv[64];
+    auto gather = [&](int j0) {  // fv[j] = H of virtual rank j0 + j when this row's adapter owns it, else 0
+        if (vec) {
+#pragma unroll
+            for (int j4 = 0; j4 < 16; ++j4) {
+                const int vv = j0 + 4 * j4;
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                if (vv >= va && vv < va + rt) x = *reinterpret_cast<const f32x4*>(hrow + (vv - va));
+                fv[4 * j4 + 0] = x[0];
+                fv[4 * j4 + 1] = x[1];
+                fv[4 * j4 + 2] = x[2];
+                fv[4 * j4 + 3] = x[3];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const int vv = j0 + j;
+                fv[j] = (vv >= va && vv < va + rt) ? hrow[vv - va] : 0.0f;
+            }
+        }
+    };
+    auto stage_f = [&]() {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                bf16 h, o;
+                split_bf16(sc * fv[c * 8 + e], h, o);
+                hi[e] = __builtin_bit_cast(uint16_t, h);
+                lo[e] = __builtin_bit_cast(uint16_t, o);
+            }
+            *reinterpret_cast<u16x8*>(shi + kmaj(tid, c)) = hi;
+            *reinterpret_cast<u16x8*>(slo + kmaj(tid, c)) = lo;
+        }
+    };
+    // virtual rank range of the adapters of each of this wave's 32-token blocks:
+    // tokens are sorted by adapter, so it runs from the first token's adapter
+    // start to the last token's adapter end (exchanged through shi, which the
+    // first chunk's F overwrites after a barrier)
+    int* vr = reinterpret_cast<int*>(shi);
+    vr[tid] = va;
+    vr[kThreads + tid] = va + ((rt + 15) & ~15);
+    lds_barrier();  // also orders the table writes before the first E loads
+    int blo[4], bhi[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int64_t b0 = q0 + (wu >> 1) * 128 + nt * 32;
+        if (b0 > tlast) {
+            blo[nt] = 1;
+            bhi[nt] = 0;
+        } else {
+            const int f = (int)(b0 - q0), e = (int)((b0 + 31 < tlast ? b0 + 31 : tlast) - q0);
+            blo[nt] = vr[f];
+            bhi[nt] = vr[kThreads + e];
+        }
+    }
+    auto chunk = [&](const uint8_t* eb, int j0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            // virtual ranks j0 + 16 kk ..: the blocks whose adapters own some of them
+            const int k0 = j0 + 16 * kk;
+            bool live[4];
+            bool any = false;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                live[nt] = blo[nt] < k0 + 16 && bhi[nt] > k0;
+                any |= live[nt];
+            }
+            if (!any) continue;
+            bf16x8 fa[4], fh[4], fl[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) fa[mt] = pfrag_tr(eb, wp * 128 + mt * 32, 16 * kk);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                if (!live[nt]) continue;
+                const int row = wq * 128 + nt * 32 + l32;
+                fh[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(shi + kmaj(row, 2 * kk + lh)));
+                fl[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(slo + kmaj(row, 2 * kk + lh)));
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                if (!live[nt]) continue;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    acc[mt][nt] = mfma32x32x16(fa[mt], fh[nt], acc[mt][nt]);
+                    acc[mt][nt] = mfma32x32x16(fa[mt], fl[nt], acc[mt][nt]);
+                }
+            }
+        }
+    };
+    // one chunk: stage F (its values are in fv), make E(c) visible, start the
+    // next chunk's loads, multiply
+    auto step = [&](uint8_t* eb, uint8_t* en, int c) {
+        const int j0 = vlo + 64 * c;
+        lds_barrier();  // every wave is done with chunk c-1 (its F tiles and the buffer en)
+        stage_f();  // its wait for fv (loaded after E(c) was issued) also covers E(c)
+        if (c + 1 < nch) {
+            issue_e(en, j0 + 64);
+            wait_vmcnt<8>();  // at most 8 loads (E(c+1)) may stay in flight
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        if (c + 1 < nch) gather(j0 + 64);
+        chunk(eb, j0);
+    };
+    issue_e(e0, vlo);
+    gather(vlo);
+    for (int c = 0; c < nch; c += 2) {
+        step(e0, e1, c);
+        if (c + 1 >= nch) break;
+        step(e1, e0, c + 1);
+    }
+}
+
 template <bool P_KMAJOR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, SegTable seg) {
     const int64_t T = a.T, K = a.K, Pdim = a.Pdim;
@@ -559,7 +747,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     lds_barrier();
 
     if (a.lora && seg.n > 0) {
-        lora_expand(acc, a, seg, q0, p0, g_t0, kBP * 2, g_w0, g_w1);
+        lora_expand_pipe(acc, a, seg, q0, p0, g_t0, g_t1, g_w0, g_w1, g_t2);
         __syncthreads();  // the expand's LDS reads are done before the staging writes
     }
     store_tile_lds(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
@@ -573,7 +761,8 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg), block(kThreads);
     const bool pipelined = a.K % 128 == 0 && a.K <= (int64_t(1) << 22) && a.Pdim <= (int64_t(1) << 22) &&
-                           a.K * a.Pdim * 2 < (int64_t(1) << 31);
+                           a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
+                           (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
     if (pipelined && p_kmajor)
         hipLaunchKernelGGL(gemm_lora_bf16_pipe<true>, grid, block, 0, st, a, s);
     else if (pipelined)

@@ -51,12 +51,14 @@ void build_segtable(const plora_desc* d, SegTable* s) {
     s->n = d->n_adapters;
     s->T = d->n_tokens;
     int64_t h = 0;
-    int32_t r = 0;
+    int32_t r = 0, v = 0;
     int32_t rmax = 0;
     for (int i = 0; i < s->n; ++i) {
         s->off[i] = d->seg_offsets[i];
         s->hoff[i] = h;
         s->roff[i] = r;
+        s->voff[i] = v;
+        v += (d->ranks[i] + 15) & ~15;
         s->rank[i] = d->ranks[i];
         s->scale[i] = d->alphas[i] / (float)d->ranks[i];
         h += (d->seg_offsets[i + 1] - d->seg_offsets[i]) * (int64_t)d->ranks[i];
@@ -66,6 +68,7 @@ void build_segtable(const plora_desc* d, SegTable* s) {
     s->off[s->n] = d->n_tokens;
     s->hoff[s->n] = h;
     s->roff[s->n] = r;
+    s->voff[s->n] = v;
     s->rmax = rmax;
 }
 

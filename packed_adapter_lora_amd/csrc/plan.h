@@ -34,6 +34,8 @@ struct SegTable {
     int64_t off[kMaxN + 1];   // segment offsets o_i
     int64_t hoff[kMaxN + 1];  // H/G block offsets: sum_{j<i} n_j r_j
     int32_t roff[kMaxN + 1];  // rank prefix R_off[i]
+    int32_t voff[kMaxN + 1];  // prefix of ranks rounded up to 16: adapter i's ranks in a
+                              // 16-aligned rank space (a k-step of 16 never spans two adapters)
     int32_t rank[kMaxN];
     float scale[kMaxN];       // alpha_i / r_i (fp32)
 };
