@@ -760,7 +760,9 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nwg), block(kThreads);
-    const bool pipelined = a.K % 128 == 0 && a.K <= (int64_t(1) << 22) && a.Pdim <= (int64_t(1) << 22) &&
+    // 32-bit buffer ranges: one tile's token rows (256 x K elements), the
+    // weight and the expand's E rows all stay below 2^31 bytes
+    const bool pipelined = a.K % 128 == 0 && a.K < (int64_t(1) << 22) && a.Pdim < (int64_t(1) << 22) &&
                            a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
                            (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
     if (pipelined && p_kmajor)
