@@ -58,6 +58,10 @@
  * last failure on the calling thread.  No C++ exception crosses this ABI.
  * Calls are reentrant; calls that share output buffers on overlapping
  * streams race, as any two kernels writing one buffer would.
+ *
+ * Environment.  PLORA_GEMM_TILE_P=128 or 256 forces the feature width of the
+ * bf16 GEMM tiles of plora_forward / plora_backward_dx (by default it is
+ * chosen per shape and device).  Results are bitwise the same either way.
  */
 #ifndef PLORA_H
 #define PLORA_H

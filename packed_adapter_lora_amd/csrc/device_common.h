@@ -90,17 +90,19 @@ __device__ __forceinline__ int tofs(int k, int c) { return k * 512 + ((c ^ ((k &
 
 typedef __bf16 bf16x4v __attribute__((vector_size(8)));
 
-// 8 consecutive rows k of column p from a tile of 512-byte rows, as one MFMA
-// operand, with two transposed LDS reads (ds_read_b64_tr_b16).  Within each
-// 16-lane group, lane L supplies the address of row kb + L/4, columns
-// pc + 4*(L%4) .. +3, and lane i gets back rows kb..kb+3 of column pc + i.
-// Lane l receives column p0 + l%32, rows kb + 8*(l/32) .. +7.
+// 8 consecutive rows k of column p from a tile of ROWB-byte rows (512 or 256;
+// 16-byte chunk c of row k stored at chunk c ^ 4 (k % 4), the tofs layout), as
+// one MFMA operand, with two transposed LDS reads (ds_read_b64_tr_b16).
+// Within each 16-lane group, lane L supplies the address of row kb + L/4,
+// columns pc + 4*(L%4) .. +3, and lane i gets back rows kb..kb+3 of column
+// pc + i.  Lane l receives column p0 + l%32, rows kb + 8*(l/32) .. +7.
+template <int ROWB = 512>
 __device__ __forceinline__ bf16x8 pfrag_tr(const uint8_t* tile, int p0, int kb) {
     const int l = lane_id(), L = l & 15, g = l >> 4;
     const int p = p0 + 16 * (g & 1) + 4 * (L & 3);
     const int k = kb + 8 * (g >> 1) + (L >> 2);
-    const uint8_t* a0 = tile + tofs(k, p >> 3) + (p & 7) * 2;
-    const uint8_t* a1 = tile + tofs(k + 4, p >> 3) + (p & 7) * 2;
+    const uint8_t* a0 = tile + k * ROWB + ((((p >> 3) ^ ((k & 3) << 2))) << 4) + (p & 7) * 2;
+    const uint8_t* a1 = tile + (k + 4) * ROWB + ((((p >> 3) ^ (((k + 4) & 3) << 2))) << 4) + (p & 7) * 2;
     typedef __attribute__((address_space(3))) bf16x4v lds_v4;
     const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a0));
     const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(a1));

@@ -29,6 +29,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <cstdlib>
+
 namespace plora {
 namespace {
 
@@ -221,15 +223,17 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Gemm
 }
 
 // The same rounding and output, staged through LDS so that global stores are
-// whole 16-byte chunks of contiguous 256-byte row pieces (one instruction = 4
-// token rows x 256 bytes) instead of 8-byte pieces of 32 rows.  Each wave
-// writes its own 128 x 128 quarter into its own 32 KiB buffer `sb` (token rows
-// of 256 bytes); 8-byte slot s of row q is stored at slot s ^ (q % 32), which
-// keeps both the 8-byte writes (32 rows, one slot) and the 16-byte reads (one
-// row, 16 chunks) free of bank conflicts.  No workgroup barrier: a wave only
-// reads what it wrote.
-__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], const GemmArgs& a, int64_t q0, int64_t p0,
+// whole 16-byte chunks of contiguous row pieces (one instruction = 1 KiB of
+// token rows) instead of 8-byte pieces of 32 rows.  Each wave writes its own
+// 128 (tokens) x 32*NM (features) quarter into its own 32 KiB buffer `sb`
+// (token rows of 64*NM bytes, NS = 8*NM slots of 8 bytes); slot s of row q is
+// stored at slot s ^ (q % NS), which keeps the 8-byte writes (rows x one slot)
+// and the 16-byte reads (one row, NS/2 chunks) free of bank conflicts.  No
+// workgroup barrier: a wave only reads what it wrote.
+template <int NM = 4>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[NM][4], const GemmArgs& a, int64_t q0, int64_t p0,
                                                uint8_t* sb) {
+    constexpr int NS = 8 * NM, RB = 8 * NS, CH = NS / 2, RPI = 64 / CH;  // slots, row bytes, chunks, rows/instr
     bf16* __restrict__ O = static_cast<bf16*>(a.O);
     const int64_t T = a.T, Pdim = a.Pdim;
     const int l = lane_id(), w = wave_id();
@@ -238,7 +242,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], const 
     for (int nt = 0; nt < 4; ++nt) {
         const int q = nt * 32 + l32;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < NM; ++mt) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 bf16x4 o;
@@ -246,18 +250,18 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[4][4], const 
                 o[1] = to_bf16(acc[mt][nt][4 * g + 1]);
                 o[2] = to_bf16(acc[mt][nt][4 * g + 2]);
                 o[3] = to_bf16(acc[mt][nt][4 * g + 3]);
-                const int slot = (mt * 8 + 2 * g + lh) ^ (q & 31);
-                *reinterpret_cast<bf16x4*>(sb + q * 256 + slot * 8) = o;
+                const int slot = (mt * 8 + 2 * g + lh) ^ (q & (NS - 1));
+                *reinterpret_cast<bf16x4*>(sb + q * RB + slot * 8) = o;
             }
         }
     }
-    const int k = l & 15;
-    const int64_t pc = p0 + wp * 128 + 8 * k;
+    const int k = l % CH;
+    const int64_t pc = p0 + wp * (32 * NM) + 8 * k;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int row = it * 4 + (l >> 4);
-        const int x = row & 31;
-        u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * 256 + ((k ^ (x >> 1)) << 4));
+    for (int it = 0; it < 128 / RPI; ++it) {
+        const int row = it * RPI + l / CH;
+        const int x = row & (NS - 1);
+        u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * RB + ((k ^ (x >> 1)) << 4));
         if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         const int64_t t = q0 + wq * 128 + row;
         if (t < T && pc < Pdim) *reinterpret_cast<u32x4*>(O + t * Pdim + pc) = v;
@@ -402,6 +406,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTab
 // ===========================================================================
 constexpr int kPipeTile = 256 * kKRow;           // 32 KiB: 256 rows x 128 B (or 64 rows x 512 B)
 
+// Tiles of p-contiguous rows (the dX weight tile, the expand's E rows) are
+// 2*BP bytes wide for a tile of BP = 64*NM features: 512 (NM = 4) or 256
+// (NM = 2) bytes.  One 1 KiB LDS DMA block holds kRowsPerBlk rows; lane l
+// fills row l / (chunks per row) of the block at physical chunk l % (chunks
+// per row), holding logical chunk (physical ^ 4 (row % 4)) -- the layout
+// pfrag_tr<2*BP> reads.
+template <int NM>
+struct PRows {
+    static_assert(NM == 4 || NM == 2, "tiles of 256 or 128 features");
+    static constexpr int kBytes = 128 * NM;               // bytes per row
+    static constexpr int kChunks = kBytes / 16;           // 16-byte chunks per row
+    static constexpr int kRowsPerBlk = 1024 / kBytes;     // 2 or 4
+    static constexpr int kShift = NM == 4 ? 5 : 4;         // log2(kChunks)
+    // row of the block this lane fills, and its byte offset within the row
+    // for a block whose first row is r0 (r0 % 4 = 0, or 2 with 2-row blocks)
+    __device__ static int lane_row(int l) { return l >> kShift; }
+    __device__ static uint32_t lane_col(int l, int r0) {
+        return (uint32_t)(((l & (kChunks - 1)) ^ ((r0 + (l >> kShift)) << 2)) << 4);
+    }
+};
+
 __shared__ __attribute__((aligned(1024))) uint8_t g_t0[kPipeTile];  // token tiles (3)
 __shared__ __attribute__((aligned(1024))) uint8_t g_t1[kPipeTile];
 __shared__ __attribute__((aligned(1024))) uint8_t g_t2[kPipeTile];
@@ -417,15 +442,31 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_w1[kPipeTile];
 // one adapter in the same grouping as when that adapter runs alone, so the
 // packed result equals the separate one bit for bit.  E rows of a chunk (p-
 // contiguous, 512 bytes) arrive by LDS DMA, double-buffered, read transposed;
-// F is block-diagonal: thread tid fills token row q0 + tid with s_i * H_i of
-// its own adapter where the chunk covers that adapter's ranks and zero
-// elsewhere (bf16 hi/lo).  The next chunk's loads are in flight during the
-// current chunk's MFMAs, and per 16-rank k-step only the 32-token blocks
-// holding tokens of the k-step's adapter multiply.  e0/e1 (E), shi/slo (F),
-// tab (virtual rank -> E row table, at most 8192 entries): 32 KiB each, free.
-__device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const GemmArgs& a, const SegTable& seg,
+// F is block-diagonal: token row t holds s_i * H_i[t] (bf16 hi + lo) at its
+// own adapter's virtual ranks and zero elsewhere.  Per 16-rank k-step only
+// the 32-token blocks holding tokens of the k-step's adapter multiply.
+//
+// F comes from one of two LDS layouts, with the same fragment values and
+// MFMA order (so the same bits):
+//  - compact (every adapter of the tile has r_i <= 64): staged once, one row
+//    per token over the token's own ranks (zero from r_i on); an MFMA lane
+//    reads the 8 ranks it needs at the adapter's local offset, or zero.  The
+//    chunks then only stream E, and each 128-token half of the tile streams
+//    its own: 32-rank chunks of its own adapters' ranks into its own half of
+//    each E buffer (the halves share at most one adapter), so both halves
+//    multiply in every step.  One barrier per step; the next step's rows are
+//    in flight during the current step's MFMAs.
+//  - per chunk (some r_i > 64): the 64 virtual ranks of the chunk for every
+//    token, restaged each chunk from registers gathered during the previous
+//    chunk.
+// e0/e1 (E), shi/slo (F hi/lo), tab (virtual rank -> E row table, at most
+// 8192 entries): 32 KiB each, free.  e1 first holds a per-token table.
+template <int NM>
+__device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const GemmArgs& a, const SegTable& seg,
                                                  int64_t q0, int64_t p0, uint8_t* e0, uint8_t* e1, uint8_t* shi,
                                                  uint8_t* slo, uint8_t* tab) {
+    using PR = PRows<NM>;
+    constexpr int RPB = PR::kRowsPerBlk;
     const int64_t T = a.T, Pdim = a.Pdim;
     const int tid = (int)threadIdx.x, l = lane_id(), w = wave_id();
     const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -440,11 +481,11 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
     const int R = seg.roff[seg.n];
     const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(static_cast<const bf16*>(a.E) + p0), 0, (int)(((int64_t)R * Pdim - p0) * 2), kRsrcWord3);
-    const int tr = l >> 5;
-    const uint32_t lane_t0 = (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
-    const uint32_t lane_t1 = (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
-    // virtual rank rows j0 .. j0+63 (those below vhi); wave: 1 KiB blocks 8w .. 8w+7 of 2
-    // rows v, v+1 (same adapter: adapters start at multiples of 16).  Padding rows read zero.
+    const int tr = PR::lane_row(l);
+    const uint32_t lane_t0 = PR::lane_col(l, 0);
+    const uint32_t lane_t1 = PR::lane_col(l, 2);  // (blocks of 2 rows starting at 2 mod 4)
+    // virtual rank rows j0 .. j0+63 (those below vhi); wave: 1 KiB blocks of RPB rows
+    // (same adapter: adapters start at multiples of 16).  Padding rows read zero.
     // Table: byte offset of the E row of virtual rank vlo + i (0x80000000 for padding: reads zero)
     const int* rowtab = reinterpret_cast<const int*>(tab);
     for (int i = i_first; i <= i_last; ++i) {
@@ -453,12 +494,13 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
             reinterpret_cast<int*>(tab)[vb + k] = k < r ? (int)((int64_t)(rb + k) * Pdim * 2) : (int)0x80000000u;
     }
     auto issue_e = [&](uint8_t* buf, int j0) {
+        constexpr int NB = 16 / RPB;  // blocks per wave: 64 rows / RPB / 4 waves
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int blk = 8 * wu + j;
-            const int v = j0 + 2 * blk;
+        for (int j = 0; j < NB; ++j) {
+            const int blk = NB * wu + j;
+            const int v = j0 + RPB * blk;
             if (v >= vhi) break;
-            const uint32_t vo = ((j & 1) ? lane_t1 : lane_t0) + (uint32_t)rowtab[v + tr - vlo];
+            const uint32_t vo = ((RPB == 2 && (j & 1)) ? lane_t1 : lane_t0) + (uint32_t)rowtab[v + tr - vlo];
             __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
     };
@@ -467,10 +509,11 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
     // The search runs over the tile's adapters with uniform indices (table reads
     // stay scalar); each lane keeps the entry that holds its token.
     const int64_t t = q0 + tid;
-    int va = 0, rt = 0;
+    int va = 0, rt = 0, rmax = 0;
     float sc = 0.0f;
     int64_t hbase = 0;
     for (int i = i_first; i <= i_last; ++i) {
+        rmax = seg.rank[i] > rmax ? seg.rank[i] : rmax;
         if (t >= seg.off[i] && t < seg.off[i + 1]) {
             va = seg.voff[i];
             rt = seg.rank[i];
@@ -478,11 +521,14 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
             hbase = seg.hoff[i] + (t - seg.off[i]) * seg.rank[i];
         }
     }
+    const bool compact = rmax <= 64;
     const float* hrow = a.F + hbase;
     // 16-byte loads need every 4-rank group to be inside or outside the row
     const bool vec = (hbase & 3) == 0 && (rt & 3) == 0;
     float fv[64];
-    auto gather = [&](int j0) {  // fv[j] = H of virtual rank j0 + j when this row's adapter owns it, else 0
+    // fv[j] = H of virtual rank j0 + j when this row's adapter owns it, else 0
+    // (compact layout: j0 = va, the row's own ranks)
+    auto gather = [&](int j0) {
         if (vec) {
 #pragma unroll
             for (int j4 = 0; j4 < 16; ++j4) {
@@ -502,6 +548,7 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
             }
         }
     };
+    // row tid of shi/slo (128-byte kmaj rows) = s * fv split into bf16 hi + lo
     auto stage_f = [&]() {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -517,98 +564,201 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[4][4], const Gemm
             *reinterpret_cast<u16x8*>(slo + kmaj(tid, c)) = lo;
         }
     };
-    // virtual rank range of the adapters of each of this wave's 32-token blocks:
-    // tokens are sorted by adapter, so it runs from the first token's adapter
-    // start to the last token's adapter end (exchanged through shi, which the
-    // first chunk's F overwrites after a barrier)
-    int* vr = reinterpret_cast<int*>(shi);
-    vr[tid] = va;
-    vr[kThreads + tid] = va + ((rt + 15) & ~15);
-    lds_barrier();  // also orders the table writes before the first E loads
-    int blo[4], bhi[4];
+    if (compact) {
+        gather(va);
+        stage_f();
+    }
+    // token table: first virtual rank of each token's adapter and the end of its
+    // 16-rank groups
+    int* ti = reinterpret_cast<int*>(e1);
+    ti[tid] = va;
+    ti[kThreads + tid] = va + ((rt + 15) & ~15);
+    lds_barrier();  // also orders the row table writes before the first E loads
+    // per MFMA lane and token block nt: the range of token wq*128 + nt*32 + l%32
+    // (compact layout); per block: the range of its adapters (tokens are sorted
+    // by adapter: first token's start to last token's end)
+    int tva[4], tve[4], blo[4], bhi[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
+        const int row = wq * 128 + nt * 32 + l32;
+        tva[nt] = ti[row];
+        tve[nt] = ti[kThreads + row];
         const int64_t b0 = q0 + (wu >> 1) * 128 + nt * 32;
         if (b0 > tlast) {
             blo[nt] = 1;
             bhi[nt] = 0;
         } else {
             const int f = (int)(b0 - q0), e = (int)((b0 + 31 < tlast ? b0 + 31 : tlast) - q0);
-            blo[nt] = vr[f];
-            bhi[nt] = vr[kThreads + e];
+            blo[nt] = ti[f];
+            bhi[nt] = ti[kThreads + e];
         }
     }
-    auto chunk = [&](const uint8_t* eb, int j0) {
+    // k-steps in pairs: both steps' fragments are read before the first
+    // step's MFMAs, so the second step's reads overlap them
+    auto chunk = [&](const uint8_t* eb, int j0, int nkk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            // virtual ranks j0 + 16 kk ..: the blocks whose adapters own some of them
-            const int k0 = j0 + 16 * kk;
-            bool live[4];
-            bool any = false;
+        for (int kp = 0; kp < 4; kp += 2) {
+            if (kp >= nkk) break;
+            bool live[2][4], any[2];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                live[nt] = blo[nt] < k0 + 16 && bhi[nt] > k0;
-                any |= live[nt];
+            for (int s2 = 0; s2 < 2; ++s2) {
+                // virtual ranks k0 ..: the blocks whose adapters own some of them
+                const int k0 = j0 + 16 * (kp + s2);
+                any[s2] = false;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    live[s2][nt] = blo[nt] < k0 + 16 && bhi[nt] > k0;
+                    any[s2] |= live[s2][nt];
+                }
             }
-            if (!any) continue;
-            bf16x8 fa[4], fh[4], fl[4];
+            bf16x8 fa[2][NM], fh[2][4], fl[2][4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) fa[mt] = pfrag_tr(eb, wp * 128 + mt * 32, 16 * kk);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (!any[s2]) continue;
+                const int kk = kp + s2, k0 = j0 + 16 * kk;
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                if (!live[nt]) continue;
-                const int row = wq * 128 + nt * 32 + l32;
-                fh[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(shi + kmaj(row, 2 * kk + lh)));
-                fl[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(slo + kmaj(row, 2 * kk + lh)));
+                for (int mt = 0; mt < NM; ++mt)
+                    fa[s2][mt] = pfrag_tr<PR::kBytes>(eb, wp * (32 * NM) + mt * 32, 16 * kk);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    if (!live[s2][nt]) continue;
+                    // ranks k0 + 8*lh .. +7 of this lane's token: 8-rank group (v - va)/8
+                    // of its compact row, or group 2*kk + lh of the chunk's rows
+                    const int v = k0 + 8 * lh;
+                    const bool own = !compact || (v >= tva[nt] && v < tve[nt]);
+                    const int col = compact ? (own ? (v - tva[nt]) >> 3 : 0) : 2 * kk + lh;
+                    const int off = kmaj(wq * 128 + nt * 32 + l32, col);
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    const u32x4 h = *reinterpret_cast<const u32x4*>(shi + off);
+                    const u32x4 o = *reinterpret_cast<const u32x4*>(slo + off);
+                    fh[s2][nt] = as_bf16x8(own ? h : z);
+                    fl[s2][nt] = as_bf16x8(own ? o : z);
+                }
             }
+            // per accumulator: k-steps in order, hi then lo (the order of the
+            // separate expand); the four accumulators of a block interleaved
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                if (!live[nt]) continue;
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (!any[s2]) continue;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    acc[mt][nt] = mfma32x32x16(fa[mt], fh[nt], acc[mt][nt]);
-                    acc[mt][nt] = mfma32x32x16(fa[mt], fl[nt], acc[mt][nt]);
+                for (int nt = 0; nt < 4; ++nt) {
+                    if (!live[s2][nt]) continue;
+#pragma unroll
+                    for (int mt = 0; mt < NM; ++mt)
+                        acc[mt][nt] = mfma32x32x16(fa[s2][mt], fh[s2][nt], acc[mt][nt]);
+#pragma unroll
+                    for (int mt = 0; mt < NM; ++mt)
+                        acc[mt][nt] = mfma32x32x16(fa[s2][mt], fl[s2][nt], acc[mt][nt]);
                 }
             }
         }
     };
-    // one chunk: stage F (its values are in fv), make E(c) visible, start the
-    // next chunk's loads, multiply
-    auto step = [&](uint8_t* eb, uint8_t* en, int c) {
-        const int j0 = vlo + 64 * c;
-        lds_barrier();  // every wave is done with chunk c-1 (its F tiles and the buffer en)
-        stage_f();  // its wait for fv (loaded after E(c) was issued) also covers E(c)
-        if (c + 1 < nch) {
-            issue_e(en, j0 + 64);
-            wait_vmcnt<8>();  // at most 8 loads (E(c+1)) may stay in flight
+    // compact layout: this half's virtual rank range (its first block's start to
+    // its last valid block's end), 32-rank chunks of it, and the step count
+    // (the larger half's chunk count, so every wave takes every barrier)
+    int hlo[2], hn[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t b0 = q0 + h * 128;
+        if (b0 > tlast) {
+            hlo[h] = 0;
+            hn[h] = 0;
         } else {
-            wait_vmcnt<0>();
+            const int f = h * 128, e = (int)((b0 + 127 < tlast ? b0 + 127 : tlast) - q0);
+            hlo[h] = __builtin_amdgcn_readfirstlane(ti[f]);
+            hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + 31) >> 5;
         }
-        lds_barrier();
-        if (c + 1 < nch) gather(j0 + 64);
-        chunk(eb, j0);
+    }
+    const int own_lo = wq ? hlo[1] : hlo[0], own_n = wq ? hn[1] : hn[0];
+    const int nstep = compact ? (hn[0] > hn[1] ? hn[0] : hn[1]) : nch;
+    // this wave's loads of its half's chunk from virtual rank j0 (32 rows, split
+    // over the wave pair: 1 KiB blocks HB*wp .. +HB-1 of RPB rows), into buf
+    // (32 rows x 128*NM bytes)
+    const int own_hi = own_lo + 32 * own_n;
+    constexpr int HB = 16 / RPB;
+    // (all table reads first, then the loads; rows past the range read zero)
+    auto issue_half = [&](uint8_t* buf, int j0) {
+        uint32_t ro[HB];
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+            const int v = j0 + RPB * (HB * wp + j);
+            const bool in = v < own_hi && v < vhi;
+            ro[j] = in ? (uint32_t)rowtab[(in ? v : vlo) + tr - vlo] : 0x80000000u;
+        }
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+            const int blk = HB * wp + j;
+            const uint32_t vo = ((RPB == 2 && (j & 1)) ? lane_t1 : lane_t0) + ro[j];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
+        }
     };
-    issue_e(e0, vlo);
-    gather(vlo);
-    for (int c = 0; c < nch; c += 2) {
+    // One chunk.  Per-chunk layout: stage F of chunk c (its values are in fv),
+    // make E(c) visible, start the next chunk's loads, multiply.  Compact
+    // layout: start the next chunk's loads, multiply, make E(c+1) visible.
+    auto step = [&](uint8_t* eb, uint8_t* en, int c) {
+        // (one chunk() call for both layouts: the accumulators stay on one path)
+        const uint8_t* ec;
+        int jc, nkk;
+        if (compact) {
+            if (c + 1 < own_n) issue_half(en + wq * (32 * PR::kBytes), own_lo + 32 * (c + 1));
+            ec = eb + wq * (32 * PR::kBytes);
+            jc = own_lo + 32 * c;
+            nkk = c < own_n ? 2 : 0;
+        } else {
+            const int j0 = vlo + 64 * c;
+            lds_barrier();  // every wave is done with chunk c-1 (its F tiles and the buffer en)
+            stage_f();      // its wait for fv (loaded after E(c) was issued) also covers E(c)
+            if (c + 1 < nch) {
+                issue_e(en, j0 + 64);
+                wait_vmcnt<8>();  // at most 8 loads (E(c+1)) may stay in flight
+            } else {
+                wait_vmcnt<0>();
+            }
+            lds_barrier();
+            if (c + 1 < nch) gather(j0 + 64);
+            ec = eb;
+            jc = j0;
+            nkk = 4;
+        }
+        chunk(ec, jc, nkk);
+        if (compact) {
+            wait_vmcnt<0>();
+            lds_barrier();  // step c+1 landed everywhere; every wave is done with eb
+        }
+    };
+    if (compact) {
+        if (own_n > 0) issue_half(e0 + wq * (32 * PR::kBytes), own_lo);
+        wait_vmcnt<0>();
+        lds_barrier();  // step 0 landed; the token table is read before step 1 overwrites it
+    } else {
+        issue_e(e0, vlo);
+        gather(vlo);
+    }
+    for (int c = 0; c < nstep; c += 2) {
         step(e0, e1, c);
-        if (c + 1 >= nch) break;
+        if (c + 1 >= nstep) break;
         step(e1, e0, c + 1);
     }
 }
 
-template <bool P_KMAJOR>
+// NM = 32-feature MFMA blocks per wave: tiles of 64*NM features x 256 tokens
+// (NM = 4: 256 x 256; NM = 2: 128 x 256, twice the tiles for shapes whose
+// 256-wide tiles leave most of the chip idle or a last partial wave).
+template <bool P_KMAJOR, int NM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, SegTable seg) {
+    constexpr int BP = 64 * NM;          // features per tile
+    constexpr int WL = 2 * NM;           // weight-tile loads per wave and stage
+    using PR = PRows<NM>;
     const int64_t T = a.T, K = a.K, Pdim = a.Pdim;
     const int tiles_q = (int)((T + kBQ - 1) / kBQ);
-    const int tiles_p = (int)((Pdim + kBP - 1) / kBP);
+    const int tiles_p = (int)((Pdim + BP - 1) / BP);
     int tq, tp;
     tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, tq, tp);
-    const int64_t q0 = (int64_t)tq * kBQ, p0 = (int64_t)tp * kBP;
+    const int64_t q0 = (int64_t)tq * kBQ, p0 = (int64_t)tp * BP;
     const int l = lane_id(), w = wave_id();
     const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
 
-    const int64_t prow = Pdim - p0 < kBP ? Pdim - p0 : kBP;
+    const int64_t prow = Pdim - p0 < BP ? Pdim - p0 : BP;
     const int64_t qrow = T - q0 < kBQ ? T - q0 : kBQ;
     // weight tile: K-contiguous rows p0.. (forward) or p-contiguous rows k.. of
     // columns p0.. (backward; columns past Pdim read neighbouring data that only
@@ -621,32 +771,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(static_cast<const bf16*>(a.Q) + q0 * K), 0, (int)(qrow * K * 2), kRsrcWord3);
     // LDS DMA block b (1 KiB).  K-contiguous tiles: 8 rows x 128 B, lane l fills
-    // row 8b + l/8, physical chunk l%8.  p-contiguous tile: 2 k-rows x 512 B, lane
-    // l fills k-row 2b + l/32, physical chunk l%32.  Wave w owns blocks 8w..8w+7.
-    // (row = 8b + l/8, so its swizzle (row ^ row/8) % 8 = (l/8 ^ b) % 8 = (l/8 ^ j) % 8)
+    // row 8b + l/8, physical chunk l%8.  p-contiguous weight tile: RPB k-rows of
+    // 2*BP bytes (PRows).  The token tile's blocks 8w..8w+7 and the weight
+    // tile's WL*w .. WL*w+WL-1 belong to wave w.
+    // (row = 8b + l/8, so its swizzle (row ^ row/8) % 8 = (l/8 ^ b) % 8)
     const int r0 = l >> 3;
     const uint32_t lane_row = (uint32_t)(r0 * K * 2);
     const uint32_t blk_stride = (uint32_t)(8 * K * 2);  // 8 rows
-    // (row k = 2b + l/32, so k%4 = 2*(b%2) + l/32: one lane offset per block parity)
-    const int tr = l >> 5;
-    const uint32_t lane_off_t0 = (uint32_t)(tr * Pdim * 2) + (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
-    const uint32_t lane_off_t1 = (uint32_t)(tr * Pdim * 2) + (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
-    const uint32_t blk_stride_t = (uint32_t)(2 * Pdim * 2);  // 2 k-rows
+    // (k-row = RPB b + row of the lane; with RPB = 2 the swizzle depends on b's parity)
+    const int tr = PR::lane_row(l);
+    const uint32_t lane_off_t0 = (uint32_t)(tr * Pdim * 2) + PR::lane_col(l, 0);
+    const uint32_t lane_off_t1 = (uint32_t)(tr * Pdim * 2) + PR::lane_col(l, 2);
+    const uint32_t blk_stride_t = (uint32_t)(PR::kRowsPerBlk * Pdim * 2);
     const int KT = (int)(K / 64);
     const int wu = __builtin_amdgcn_readfirstlane(w);  // wave-uniform: LDS DMA bases stay scalar
     // past the last stage: push the offset beyond the resource's range (all
     // ranges are < 2^31 bytes), so the load writes zeros; no branch
     auto oob = [&](int kt) { return kt < KT ? 0u : 0x80000000u; };
-    // this wave's 8 loads of stage kt's weight tile / token tile
+    // this wave's WL (weight) / 8 (token) loads of stage kt
     auto issue_w = [&](uint8_t* buf, int kt) {
         const uint32_t kb = (uint32_t)kt * 128u + oob(kt);
         const uint32_t kbt = (uint32_t)kt * (uint32_t)(64 * Pdim * 2) + oob(kt);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int blk = 8 * wu + j;
+        for (int j = 0; j < WL; ++j) {
+            const int blk = WL * wu + j;
             const uint32_t vo =
-                P_KMAJOR ? lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ j) & 7)) << 4) + (uint32_t)blk * blk_stride + kb
-                         : ((j & 1) ? lane_off_t1 : lane_off_t0) + (uint32_t)blk * blk_stride_t + kbt;
+                P_KMAJOR ? lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * blk_stride + kb
+                         : ((PR::kRowsPerBlk == 2 && (j & 1)) ? lane_off_t1 : lane_off_t0) +
+                               (uint32_t)blk * blk_stride_t + kbt;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
     };
@@ -660,19 +812,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[NM][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NM; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    bf16x8 fa[2][4], fb[2][4];
+    bf16x8 fa[2][NM], fb[2][4];
     auto rd = [&](const uint8_t* bw, const uint8_t* bt, int kk, int s) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < NM; ++m) {
             if constexpr (P_KMAJOR)
-                fa[s][m] = as_bf16x8(*reinterpret_cast<const u32x4*>(bw + kmaj(wp * 128 + m * 32 + l32, 2 * kk + lh)));
+                fa[s][m] =
+                    as_bf16x8(*reinterpret_cast<const u32x4*>(bw + kmaj(wp * (32 * NM) + m * 32 + l32, 2 * kk + lh)));
             else
-                fa[s][m] = pfrag_tr(bw, wp * 128 + m * 32, 16 * kk);  // p-contiguous weight tile
+                fa[s][m] = pfrag_tr<PR::kBytes>(bw, wp * (32 * NM) + m * 32, 16 * kk);  // p-contiguous weight tile
         }
 #pragma unroll
         for (int n = 0; n < 4; ++n)
@@ -680,18 +833,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     };
     auto mm = [&](int s) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < NM; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n) acc[m][n] = mfma32x32x16(fa[s][m], fb[s][n], acc[m][n]);
     };
-    // 16 MFMAs interleaved with 8 fragment reads (and `dma` LDS DMA loads)
+    // 4*NM MFMAs interleaved with NM + 4 fragment reads (and `dma` LDS DMA loads)
     auto sched = [&](int dma) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // LDS DMA load
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (2 * i < 4 * NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (i < NM + 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+            if (i < dma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // LDS DMA load
+            if (2 * i + 1 < 4 * NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -715,14 +868,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
         issue_w(wc, kt + 2);
         rd(wn, tn, 0, 0);
         mm(1);
-        sched(8);
+        sched(WL);
     };
 
     issue_t(g_t0, 0);
     issue_w(g_w0, 0);
     issue_t(g_t1, 1);
     issue_w(g_w1, 1);
-    wait_vmcnt<16>();
+    wait_vmcnt<8 + WL>();  // stage 0 landed (stage 1 may be in flight)
     lds_barrier();
     rd(g_w0, g_t0, 0, 0);
     int kt = 0;
@@ -747,32 +900,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     lds_barrier();
 
     if (a.lora && seg.n > 0) {
-        lora_expand_pipe(acc, a, seg, q0, p0, g_t0, g_t1, g_w0, g_w1, g_t2);
+        lora_expand_pipe<NM>(acc, a, seg, q0, p0, g_t0, g_t1, g_w0, g_w1, g_t2);
         __syncthreads();  // the expand's LDS reads are done before the staging writes
     }
-    store_tile_lds(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
+    store_tile_lds<NM>(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
 }
 }  // namespace
+
+// Compute units of the current device (cached per device id).
+static int cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st) {
     const int64_t tq = (a.T + kBQ - 1) / kBQ, tp = (a.Pdim + kBP - 1) / kBP;
     const int64_t nwg = tq * tp;
     if (nwg <= 0) return hipSuccess;
-    if (nwg > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nwg), block(kThreads);
+    if (nwg > 0x3fffffff) return hipErrorInvalidValue;
+    const dim3 block(kThreads);
     // 32-bit buffer ranges: one tile's token rows (256 x K elements), the
     // weight and the expand's E rows all stay below 2^31 bytes
     const bool pipelined = a.K % 128 == 0 && a.K < (int64_t(1) << 22) && a.Pdim < (int64_t(1) << 22) &&
                            a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
                            (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
-    if (pipelined && p_kmajor)
-        hipLaunchKernelGGL(gemm_lora_bf16_pipe<true>, grid, block, 0, st, a, s);
-    else if (pipelined)
-        hipLaunchKernelGGL(gemm_lora_bf16_pipe<false>, grid, block, 0, st, a, s);
-    else if (p_kmajor)
-        hipLaunchKernelGGL(gemm_lora_bf16<true>, grid, block, 0, st, a, s);
-    else
-        hipLaunchKernelGGL(gemm_lora_bf16<false>, grid, block, 0, st, a, s);
+    if (pipelined) {
+        // 128-wide tiles when all of them fit on the chip at once (a few hundred
+        // tokens): each takes ~0.57 of a 256-wide tile's time.  With more tiles
+        // than CUs the 256-wide ones win, partial last waves included (fewer
+        // busy CUs run at a higher clock).  PLORA_GEMM_TILE_P=128 or 256 forces
+        // the width (same results either way: each output element sees the same
+        // MFMA sequence).
+        const int64_t cus = cu_count(), nwg2 = tq * ((a.Pdim + 127) / 128);
+        const char* force = getenv("PLORA_GEMM_TILE_P");
+        const int fw = force ? atoi(force) : 0;
+        const bool half = fw == 128 || (fw != 256 && nwg2 <= cus);
+        const dim3 grid((unsigned)(half ? nwg2 : nwg));
+        if (p_kmajor && half)
+            hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 2>), grid, block, 0, st, a, s);
+        else if (p_kmajor)
+            hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 4>), grid, block, 0, st, a, s);
+        else if (half)
+            hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 2>), grid, block, 0, st, a, s);
+        else
+            hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4>), grid, block, 0, st, a, s);
+    } else {
+        const dim3 grid((unsigned)nwg);
+        if (p_kmajor)
+            hipLaunchKernelGGL(gemm_lora_bf16<true>, grid, block, 0, st, a, s);
+        else
+            hipLaunchKernelGGL(gemm_lora_bf16<false>, grid, block, 0, st, a, s);
+    }
     return hipGetLastError();
 }
 

@@ -57,22 +57,53 @@ def test_bf16_ragged_full(P):
     full_case(P, wl)
 
 
-def test_bf16_multitile_full(P):
+# The pipelined bf16 GEMM has 256- and 128-feature tiles, chosen per shape
+# (PLORA_GEMM_TILE_P forces one): the shapes below run under both.
+TILE_WIDTHS = pytest.mark.parametrize("tile_p", ["256", "128"])
+
+
+@TILE_WIDTHS
+def test_bf16_multitile_full(P, tile_p, monkeypatch):
+    monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
     wl = workloads.custom(512, 768, [700, 5, 0, 395], [16, 8, 32, 64], [32.0, 16.0, 8.0, 16.0], "bf16",
                           seed=22, name="multitile_bf16")
     full_case(P, wl)
 
 
-def test_bf16_pipelined_tails_full(P):
+@TILE_WIDTHS
+def test_bf16_pipelined_tails_full(P, tile_p, monkeypatch):
     # pipelined GEMMs (K % 128 == 0 both ways) with a feature tail in both
-    # orientations (640 % 256, 384 % 256) and a token tail (777 % 256)
+    # orientations (640 % 256 and % 128, 384 % 256) and a token tail (777 % 256)
+    monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
     wl = workloads.custom(384, 640, [100, 0, 513, 1, 163], [16, 8, 64, 32, 1], [32.0, 16.0, 8.0, 16.0, 4.0],
                           "bf16", seed=29, name="pipe_tails_bf16")
     full_case(P, wl)
 
 
-def test_max_adapters_and_rank(P):
+# (384, 704): pipelined forward with a feature tail at either width (704 % 256,
+# 704 % 128); (712, 640): the same for the backward GEMM (d_in = 712).
+@pytest.mark.parametrize("d_in,d_out", [(384, 704), (712, 640)])
+def test_tile_widths_bitwise_equal(P, d_in, d_out, monkeypatch):
+    """Both tile widths give every output element the same MFMA sequence: equal bits."""
+    import torch
+    wl = workloads.custom(d_in, d_out, [100, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
+                          [32.0, 16.0, 8.0, 16.0, 4.0, 256.0], "bf16", seed=31, name="tile_widths")
+    log("case %s" % wl.name)
+    inp = workloads.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    out = {}
+    for tile_p in ("256", "128"):
+        monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
+        out[tile_p] = run_gpu(P, wl, dev)
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    for k in ("Y", "dX"):
+        assert torch.equal(bits(out["256"][k]), bits(out["128"][k])), k
+
+
+@TILE_WIDTHS
+def test_max_adapters_and_rank(P, tile_p, monkeypatch):
     # 64 adapters (the ABI maximum), ranks up to 128 (the maximum), empty and 1-token segments
+    monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
     n = 64
     counts = [(i * 37) % 97 if i % 9 else 0 for i in range(n)]
     counts[5] = 1
@@ -196,9 +227,11 @@ def test_reproducible_bitwise(P):
 
 
 @pytest.mark.parametrize("d_in,d_out", [(320, 1032), (512, 768)])
-def test_packed_equals_separate_bitwise(P, d_in, d_out):
+@TILE_WIDTHS
+def test_packed_equals_separate_bitwise(P, d_in, d_out, tile_p, monkeypatch):
     """The packed call gives each adapter exactly what a call with that adapter alone gives."""
     import torch
+    monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
     wl = workloads.custom(d_in, d_out, [129, 0, 2200, 31, 600], [16, 8, 64, 1, 33], [32.0, 16.0, 8.0, 2.0, 66.0],
                           "bf16", seed=28, name="packed_vs_separate")
     log("case %s" % wl.name)

@@ -115,7 +115,7 @@ def config(name: str, n_adapters: int | None = None, tokens_each: int | None = N
     decode_up, decode_sq
               decode-shaped serving batches on the llama_up / llama_sq
               shapes: N adapters (default 64) with 1, 2, 4, 8, 16 tokens
-              (cycling; 397 tokens at N = 64), ranks cycle 8..64
+              (cycling; 387 tokens at N = 64), ranks cycle 8..64
     """
     if name == "tiny":
         return Workload("tiny", 256, 256, _offsets([64, 64]), np.array([4, 8], np.int32),
