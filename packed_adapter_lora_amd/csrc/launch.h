@@ -30,6 +30,8 @@ struct ShrinkArgs {
     const void* P;   // [R][K]
     float* out;      // H or G
     int64_t K;
+    void* scratch;       // output activation (Y or dX), free until the GEMM writes it
+    int64_t scratch_row; // its bytes per token row (0: no K slices)
 };
 
 // Weight gradient: out[R_off[i]+j][c] = s_i sum_{t in S_i} F_i[t-o_i][j] Q[t][c]

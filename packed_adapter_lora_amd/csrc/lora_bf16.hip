@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 
 // ---------------------------------------------------------------------------
 // Pipelined shrink (K a multiple of 64): one workgroup per 128-token tile of
-// one adapter.  Each 64-k stage brings the tile's 128 rows of X/dY and the
+// one adapter, or per K slice of it (shrink_slices: adapters of a few tokens,
+// whose single tile would otherwise walk all of K on one CU).  Each 64-k stage brings the tile's 128 rows of X/dY and the
 // adapter's 32*MAXJT panel rows into LDS with LDS DMA (1 KiB per instruction =
 // 8 rows x 128 B, whole cache lines), three stages deep so two stay in flight;
 // wavefront w multiplies its 32 token rows against the panel.  Rows past the
@@ -124,11 +125,13 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
 
 template <int MAXJT>
 __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
-    const int tile = (int)blockIdx.x;
+    const int unit = (int)blockIdx.x;
     const int64_t K = a.K;
-    const int i = adapter_of_unit(m, seg.n, tile);
+    const int i = adapter_of_unit(m, seg.n, unit);
     const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
-    const int64_t t0 = s0 + (int64_t)(tile - m.pre[i]) * kShrinkTileRows;
+    const int nsl = shrink_slices(s1 - s0, seg.rank[i], K, a.scratch_row);
+    const int u = unit - m.pre[i], slice = u % nsl;
+    const int64_t t0 = s0 + (int64_t)(u / nsl) * kShrinkTileRows;
     const int nrows = (int)(s1 - t0 < kShrinkTileRows ? s1 - t0 : kShrinkTileRows);
     const int r = seg.rank[i];
     const int ntj = (r + 31) >> 5;
@@ -142,10 +145,11 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
     // DMA block b: rows 8b .. 8b+7; lane l -> row 8b + l/8, physical chunk l%8
     const int r0 = l >> 3;
     const uint32_t lane_row = (uint32_t)(r0 * K * 2);
-    const int KT = (int)(K / 64);
+    // this work item's stages: [kt0, kt1) of the K / 64
+    const int KT = (int)(K / 64), kt0 = slice * KT / nsl, kt1 = (slice + 1) * KT / nsl;
     // token tile: blocks 4w .. 4w+3 (16 blocks = 128 rows); panel: blocks MAXJT*w .. (4*MAXJT blocks)
     auto issue = [&](uint8_t* buf, int kt) {
-        const uint32_t oob = kt < KT ? 0u : 0x80000000u;
+        const uint32_t oob = kt < kt1 ? 0u : 0x80000000u;
         const uint32_t kb = (uint32_t)kt * 128u + oob;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -183,19 +187,24 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
         issue(prv, kt + 2);
         compute(cur);
     };
-    issue(g_sh0, 0);
-    issue(g_sh1, 1);
-    for (int kt = 0; kt < KT; kt += 3) {
+    issue(g_sh0, kt0);
+    issue(g_sh1, kt0 + 1);
+    for (int kt = kt0; kt < kt1; kt += 3) {
         step(g_sh0, g_sh2, kt);
-        if (kt + 1 >= KT) break;
+        if (kt + 1 >= kt1) break;
         step(g_sh1, g_sh0, kt + 1);
-        if (kt + 2 >= KT) break;
+        if (kt + 2 >= kt1) break;
         step(g_sh2, g_sh1, kt + 2);
     }
     wait_vmcnt<0>();
 
-    // D[t][j]: lane holds rank column j, token rows 8*(v/4) + 4*(l/32) + v%4 of its wave's 32
-    float* __restrict__ out = a.out + seg.hoff[i] + (t0 - s0) * r;
+    // D[t][j]: lane holds rank column j, token rows 8*(v/4) + 4*(l/32) + v%4 of its wave's 32.
+    // K slices: slice s of the adapter's [n_i][r_i] block goes to its own rows of
+    // the scratch activation, s * n_i * r_i floats in (shrink_slice_sum adds them)
+    float* __restrict__ out =
+        nsl == 1 ? a.out + seg.hoff[i] + (t0 - s0) * r
+                 : reinterpret_cast<float*>(static_cast<uint8_t*>(a.scratch) + s0 * a.scratch_row) +
+                       (int64_t)slice * (s1 - s0) * r;
 #pragma unroll
     for (int jt = 0; jt < MAXJT; ++jt) {
         const int j = jt * 32 + l32;
@@ -541,31 +550,54 @@ __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, W
     }
 }
 
+// Sum of the K slices of the shrink (fixed order 0, 1, ...) into H / G: one
+// workgroup per adapter; adapters that were not sliced return at once.
+__global__ __launch_bounds__(256) void shrink_slice_sum(ShrinkArgs a, SegTable seg) {
+    const int i = (int)blockIdx.x;
+    const int64_t n = seg.off[i + 1] - seg.off[i];
+    const int r = seg.rank[i];
+    const int nsl = shrink_slices(n, r, a.K, a.scratch_row);
+    if (nsl == 1) return;
+    const int64_t ne = n * r;
+    const float* __restrict__ part =
+        reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.scratch) + seg.off[i] * a.scratch_row);
+    float* __restrict__ out = a.out + seg.hoff[i];
+    for (int64_t e = threadIdx.x; e < ne; e += 256) {
+        float v = part[e];
+        for (int sl = 1; sl < nsl; ++sl) v += part[sl * ne + e];
+        out[e] = v;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
+hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st) {
     if (units <= 0) return hipSuccess;
-    if (a.K % 64 == 0 && (int64_t)kShrinkTileRows * a.K * 2 < (int64_t(1) << 31) &&
-        (int64_t)s.roff[s.n] * a.K * 2 < (int64_t(1) << 31)) {
+    if (a_in.K % 64 == 0 && (int64_t)kShrinkTileRows * a_in.K * 2 < (int64_t(1) << 31) &&
+        (int64_t)s.roff[s.n] * a_in.K * 2 < (int64_t(1) << 31)) {
+        ShrinkArgs a = a_in;
+        if (!a.scratch) a.scratch_row = 0;
         WorkMap m128;
-        const int32_t tiles = build_shrink_map(s, &m128, kShrinkTileRows);
-        const dim3 grid((unsigned)tiles), block(256);
+        bool split = false;
+        const int32_t items = build_shrink_pipe_map(s, &m128, a.K, a.scratch_row, &split);
+        const dim3 grid((unsigned)items), block(256);
         switch ((s.rmax + 31) / 32) {
             case 1: hipLaunchKernelGGL(shrink_bf16_pipe<1>, grid, block, 0, st, a, s, m128); break;
             case 2: hipLaunchKernelGGL(shrink_bf16_pipe<2>, grid, block, 0, st, a, s, m128); break;
             case 3: hipLaunchKernelGGL(shrink_bf16_pipe<3>, grid, block, 0, st, a, s, m128); break;
             default: hipLaunchKernelGGL(shrink_bf16_pipe<4>, grid, block, 0, st, a, s, m128); break;
         }
+        if (split) hipLaunchKernelGGL(shrink_slice_sum, dim3((unsigned)s.n), block, 0, st, a, s);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
     const int jt = (s.rmax + 31) / 32;
     switch (jt) {
-        case 1: hipLaunchKernelGGL(shrink_bf16<1>, grid, block, 0, st, a, s, m, units); break;
-        case 2: hipLaunchKernelGGL(shrink_bf16<2>, grid, block, 0, st, a, s, m, units); break;
-        case 3: hipLaunchKernelGGL(shrink_bf16<3>, grid, block, 0, st, a, s, m, units); break;
-        default: hipLaunchKernelGGL(shrink_bf16<4>, grid, block, 0, st, a, s, m, units); break;
+        case 1: hipLaunchKernelGGL(shrink_bf16<1>, grid, block, 0, st, a_in, s, m, units); break;
+        case 2: hipLaunchKernelGGL(shrink_bf16<2>, grid, block, 0, st, a_in, s, m, units); break;
+        case 3: hipLaunchKernelGGL(shrink_bf16<3>, grid, block, 0, st, a_in, s, m, units); break;
+        default: hipLaunchKernelGGL(shrink_bf16<4>, grid, block, 0, st, a_in, s, m, units); break;
     }
     return hipGetLastError();
 }

@@ -83,6 +83,20 @@ int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows) {
     return t;
 }
 
+int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split) {
+    int32_t t = 0;
+    *any_split = false;
+    for (int i = 0; i < s.n; ++i) {
+        m->pre[i] = t;
+        const int64_t ni = s.off[i + 1] - s.off[i];
+        const int sl = shrink_slices(ni, s.rank[i], K, row_bytes);
+        *any_split = *any_split || sl > 1;
+        t += (int32_t)((ni + kShrinkTileRows - 1) / kShrinkTileRows) * sl;
+    }
+    m->pre[s.n] = t;
+    return t;
+}
+
 int32_t wgrad_chunk_tokens(int64_t D) { return D > 8192 ? 2048 : 1024; }
 
 void build_wgrad_plan(const SegTable& s, int64_t D, WgradPlan* p) {

@@ -69,6 +69,26 @@ void build_segtable(const plora_desc* d, SegTable* s);
 // Shrink tiles: ceil(n_i / rows) per adapter.  Returns the total.
 int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows = kShrinkRows);
 
+// K slices of the pipelined shrink for adapter i (n tokens, rank r) over K:
+// an adapter with a single 128-token tile is split over kShrinkSlices
+// workgroups along K when the slices' fp32 partials (kShrinkSlices x n x r)
+// fit in its own rows of the output activation (row_bytes bytes per token;
+// 0 = no scratch), which the GEMM overwrites afterwards; the partials are then
+// added in slice order.  It depends on the adapter alone, so packed and
+// separate calls sum in the same order.
+constexpr int kShrinkSlices = 4;
+constexpr int shrink_slices(int64_t n, int r, int64_t K, int64_t row_bytes) {
+    return (row_bytes > 0 && n >= 1 && n <= kShrinkTileRows && K % 64 == 0 && K / 64 >= 2 * kShrinkSlices &&
+            (int64_t)4 * kShrinkSlices * r <= row_bytes)
+               ? kShrinkSlices
+               : 1;
+}
+
+// Work items of the pipelined shrink: tiles of 128 tokens x shrink_slices()
+// per adapter.  Returns the total; *any_split tells whether a partial sum
+// pass is needed.
+int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split);
+
 // Token-chunk size of the weight-gradient reduction over a feature width D.
 // It depends only on D, so an adapter's reduction order is the same whether
 // it is packed with others or run alone.
