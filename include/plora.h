@@ -117,12 +117,15 @@ typedef struct {
 } plora_desc;
 
 /* Forward: Y = X W_m + concat_i[ s_i (X[S_i] A_i) B_i ], and H (fp32) for the
- * weight-gradient pass.  Y and H are overwritten. */
+ * weight-gradient pass.  Y and H are overwritten; Y must not overlap any
+ * input, since the call may first use an adapter's own rows of Y as scratch
+ * (partial sums of H) before writing the result there. */
 int plora_forward(const plora_desc* desc, const void* X, const void* W, const void* A,
                   const void* B, void* Y, float* H, void* stream);
 
 /* Backward through the activations: dX = dY W_m^T + concat_i[ s_i G_i A_i^T ]
- * with G_i = dY[S_i] B_i^T, and G (fp32) for the weight-gradient pass. */
+ * with G_i = dY[S_i] B_i^T, and G (fp32) for the weight-gradient pass.  dX
+ * and G are overwritten; dX must not overlap any input (scratch as for Y). */
 int plora_backward_dx(const plora_desc* desc, const void* dY, const void* W, const void* A,
                       const void* B, void* dX, float* G, void* stream);
 
