@@ -60,13 +60,6 @@ __device__ __forceinline__ int segment_of(const SegTable& s, int64_t t) {
     return lo;
 }
 
-// The same search restricted to adapters i0 .. i1 (i0's segment starts at or before t).
-__device__ __forceinline__ int segment_in(const SegTable& s, int i0, int i1, int64_t t) {
-    int i = i0;
-    while (i < i1 && s.off[i + 1] <= t) ++i;
-    return i;
-}
-
 // Work map lookup: the i with pre[i] <= w < pre[i+1].
 __device__ __forceinline__ int adapter_of_unit(const WorkMap& m, int n, int32_t w) {
     int i = 0;

@@ -452,10 +452,11 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_w1[kPipeTile];
 //    per token over the token's own ranks (zero from r_i on); an MFMA lane
 //    reads the 8 ranks it needs at the adapter's local offset, or zero.  The
 //    chunks then only stream E, and each 128-token half of the tile streams
-//    its own: 32-rank chunks of its own adapters' ranks into its own half of
-//    each E buffer (the halves share at most one adapter), so both halves
-//    multiply in every step.  One barrier per step; the next step's rows are
-//    in flight during the current step's MFMAs.
+//    its own: chunks of its own adapters' ranks (32 rows of 512 bytes, or 64
+//    of 256 with 128-feature tiles: 16 KiB) into its own half of each E
+//    buffer (the halves share at most one adapter), so both halves multiply
+//    in every step.  One barrier per step; the next step's rows are in flight
+//    during the current step's MFMAs.
 //  - per chunk (some r_i > 64): the 64 virtual ranks of the chunk for every
 //    token, restaged each chunk from registers gathered during the previous
 //    chunk.
@@ -472,7 +473,11 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
     const int64_t tlast = (q0 + kBQ < T ? q0 + kBQ : T) - 1;
-    const int i_first = segment_of(seg, q0), i_last = segment_in(seg, i_first, seg.n - 1, tlast);
+    // The tile's adapters: the first whose segment ends past q0, the first
+    // whose segment ends past tlast (lane j tests adapter j; at most 64)
+    const int64_t endl = l < seg.n ? seg.off[l + 1] : INT64_MAX;
+    const int i_first = (int)__popcll(__ballot(endl <= q0));
+    const int i_last = (int)__popcll(__ballot(endl <= tlast));
     const int vlo = seg.voff[i_first], vhi = seg.voff[i_last + 1];
     const int nch = (vhi - vlo + 63) >> 6;
     if (nch <= 0) return;
@@ -488,11 +493,6 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
     // (same adapter: adapters start at multiples of 16).  Padding rows read zero.
     // Table: byte offset of the E row of virtual rank vlo + i (0x80000000 for padding: reads zero)
     const int* rowtab = reinterpret_cast<const int*>(tab);
-    for (int i = i_first; i <= i_last; ++i) {
-        const int vb = seg.voff[i] - vlo, vn = seg.voff[i + 1] - seg.voff[i], r = seg.rank[i], rb = seg.roff[i];
-        for (int k = tid; k < vn; k += kThreads)
-            reinterpret_cast<int*>(tab)[vb + k] = k < r ? (int)((int64_t)(rb + k) * Pdim * 2) : (int)0x80000000u;
-    }
     auto issue_e = [&](uint8_t* buf, int j0) {
         constexpr int NB = 16 / RPB;  // blocks per wave: 64 rows / RPB / 4 waves
 #pragma unroll
@@ -505,21 +505,64 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
 
-    // this thread's token row: adapter, its virtual rank range, its H row and scale.
-    // The search runs over the tile's adapters with uniform indices (table reads
-    // stay scalar); each lane keeps the entry that holds its token.
+    // Per-adapter records of the tile's adapters (in e1 past the token table,
+    // free until the E loads of step 1): lane j of wave 0 takes adapter
+    // i_first + j, writes its E row table entries (virtual rank -> byte
+    // offset, at most 128 per adapter) and its record; the largest rank goes
+    // into the record area too.
+    const int na = i_last - i_first + 1;
+    int64_t* rec_off = reinterpret_cast<int64_t*>(e1 + 4096);  // 64 x 8 B
+    int64_t* rec_hoff = rec_off + 64;                          // 64 x 8 B
+    int* rec_voff = reinterpret_cast<int*>(rec_hoff + 64);     // 64 x 4 B
+    int* rec_rank = rec_voff + 64;
+    float* rec_scale = reinterpret_cast<float*>(rec_rank + 64);
+    int* rec_rmax = reinterpret_cast<int*>(rec_scale + 64);
+    if (wu == 0) {
+        const int i = i_first + l;
+        int r = 0;
+        if (l < na) {
+            const int v0 = seg.voff[i], vn = seg.voff[i + 1] - v0, rb = seg.roff[i];
+            r = seg.rank[i];
+            // (16 entries per iteration: vn and v0 - vlo are multiples of 16)
+            for (int k = 0; k < vn; k += 16) {
+                u32x4 e[4];
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    e[q >> 2][q & 3] = k + q < r ? (uint32_t)((int64_t)(rb + k + q) * Pdim * 2) : 0x80000000u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(tab)[(v0 - vlo + k) / 4 + q] = e[q];
+            }
+            rec_off[l] = seg.off[i];
+            rec_hoff[l] = seg.hoff[i];
+            rec_voff[l] = v0;
+            rec_rank[l] = r;
+            rec_scale[l] = seg.scale[i];
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const int o = __shfl_xor(r, d);
+            r = o > r ? o : r;
+        }
+        if (l == 0) *rec_rmax = r;
+    }
+    lds_barrier();
+    // this thread's token row: its adapter (the last record starting at or
+    // before it), the adapter's virtual rank range, its H row and scale
     const int64_t t = q0 + tid;
-    int va = 0, rt = 0, rmax = 0;
+    const int rmax = __builtin_amdgcn_readfirstlane(*rec_rmax);
+    int va = 0, rt = 0;
     float sc = 0.0f;
     int64_t hbase = 0;
-    for (int i = i_first; i <= i_last; ++i) {
-        rmax = seg.rank[i] > rmax ? seg.rank[i] : rmax;
-        if (t >= seg.off[i] && t < seg.off[i + 1]) {
-            va = seg.voff[i];
-            rt = seg.rank[i];
-            sc = seg.scale[i];
-            hbase = seg.hoff[i] + (t - seg.off[i]) * seg.rank[i];
+    if (t <= tlast) {
+        int lo = 0, hi = na;  // rec_off[lo] <= t < rec_off[hi] (or hi == na)
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (rec_off[mid] <= t) lo = mid; else hi = mid;
         }
+        va = rec_voff[lo];
+        rt = rec_rank[lo];
+        sc = rec_scale[lo];
+        hbase = rec_hoff[lo] + (t - rec_off[lo]) * rt;
     }
     const bool compact = rmax <= 64;
     const float* hrow = a.F + hbase;
@@ -654,8 +697,9 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
     // compact layout: this half's virtual rank range (its first block's start to
-    // its last valid block's end), 32-rank chunks of it, and the step count
+    // its last valid block's end), HR-rank chunks of it, and the step count
     // (the larger half's chunk count, so every wave takes every barrier)
+    constexpr int HR = 16384 / PR::kBytes;  // 32 or 64 rows: 16 KiB per half
     int hlo[2], hn[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -666,16 +710,16 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         } else {
             const int f = h * 128, e = (int)((b0 + 127 < tlast ? b0 + 127 : tlast) - q0);
             hlo[h] = __builtin_amdgcn_readfirstlane(ti[f]);
-            hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + 31) >> 5;
+            hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + HR - 1) / HR;
         }
     }
     const int own_lo = wq ? hlo[1] : hlo[0], own_n = wq ? hn[1] : hn[0];
     const int nstep = compact ? (hn[0] > hn[1] ? hn[0] : hn[1]) : nch;
-    // this wave's loads of its half's chunk from virtual rank j0 (32 rows, split
+    // this wave's loads of its half's chunk from virtual rank j0 (HR rows, split
     // over the wave pair: 1 KiB blocks HB*wp .. +HB-1 of RPB rows), into buf
-    // (32 rows x 128*NM bytes)
-    const int own_hi = own_lo + 32 * own_n;
-    constexpr int HB = 16 / RPB;
+    // (16 KiB)
+    const int own_hi = own_lo + HR * own_n;
+    constexpr int HB = 8;
     // (all table reads first, then the loads; rows past the range read zero)
     auto issue_half = [&](uint8_t* buf, int j0) {
         uint32_t ro[HB];
@@ -700,10 +744,10 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         const uint8_t* ec;
         int jc, nkk;
         if (compact) {
-            if (c + 1 < own_n) issue_half(en + wq * (32 * PR::kBytes), own_lo + 32 * (c + 1));
-            ec = eb + wq * (32 * PR::kBytes);
-            jc = own_lo + 32 * c;
-            nkk = c < own_n ? 2 : 0;
+            if (c + 1 < own_n) issue_half(en + wq * 16384, own_lo + HR * (c + 1));
+            ec = eb + wq * 16384;
+            jc = own_lo + HR * c;
+            nkk = c < own_n ? HR / 16 : 0;
         } else {
             const int j0 = vlo + 64 * c;
             lds_barrier();  // every wave is done with chunk c-1 (its F tiles and the buffer en)
@@ -727,7 +771,7 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
     if (compact) {
-        if (own_n > 0) issue_half(e0 + wq * (32 * PR::kBytes), own_lo);
+        if (own_n > 0) issue_half(e0 + wq * 16384, own_lo);
         wait_vmcnt<0>();
         lds_barrier();  // step 0 landed; the token table is read before step 1 overwrites it
     } else {
