@@ -607,9 +607,13 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
             *reinterpret_cast<u16x8*>(slo + kmaj(tid, c)) = lo;
         }
     };
+    // 16 zero bytes past the row table (compact: at most 64 x 64 entries = 16 KiB):
+    // the F fragment of lanes whose token does not own the k-step's ranks
+    const uint8_t* zero16 = tab + 32768 - 16;
     if (compact) {
         gather(va);
         stage_f();
+        if (tid == 0) *reinterpret_cast<u32x4*>(tab + 32768 - 16) = u32x4{0u, 0u, 0u, 0u};
     }
     // token table: first virtual rank of each token's adapter and the end of its
     // 16-rank groups
@@ -632,8 +636,8 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
             bhi[nt] = 0;
         } else {
             const int f = (int)(b0 - q0), e = (int)((b0 + 31 < tlast ? b0 + 31 : tlast) - q0);
-            blo[nt] = ti[f];
-            bhi[nt] = ti[kThreads + e];
+            blo[nt] = __builtin_amdgcn_readfirstlane(ti[f]);  // (wave-uniform: scalar tests below)
+            bhi[nt] = __builtin_amdgcn_readfirstlane(ti[kThreads + e]);
         }
     }
     // k-steps in pairs: both steps' fragments are read before the first
@@ -667,15 +671,13 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
                     if (!live[s2][nt]) continue;
                     // ranks k0 + 8*lh .. +7 of this lane's token: 8-rank group (v - va)/8
                     // of its compact row, or group 2*kk + lh of the chunk's rows
+                    // (lanes that do not own them read 16 zero bytes)
                     const int v = k0 + 8 * lh;
                     const bool own = !compact || (v >= tva[nt] && v < tve[nt]);
                     const int col = compact ? (own ? (v - tva[nt]) >> 3 : 0) : 2 * kk + lh;
                     const int off = kmaj(wq * 128 + nt * 32 + l32, col);
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    const u32x4 h = *reinterpret_cast<const u32x4*>(shi + off);
-                    const u32x4 o = *reinterpret_cast<const u32x4*>(slo + off);
-                    fh[s2][nt] = as_bf16x8(own ? h : z);
-                    fl[s2][nt] = as_bf16x8(own ? o : z);
+                    fh[s2][nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(own ? shi + off : zero16));
+                    fl[s2][nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(own ? slo + off : zero16));
                 }
             }
             // per accumulator: k-steps in order, hi then lo (the order of the
@@ -713,7 +715,8 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
             hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + HR - 1) / HR;
         }
     }
-    const int own_lo = wq ? hlo[1] : hlo[0], own_n = wq ? hn[1] : hn[0];
+    const int wqu = wu >> 1;  // (this wave's half, wave-uniform)
+    const int own_lo = wqu ? hlo[1] : hlo[0], own_n = wqu ? hn[1] : hn[0];
     const int nstep = compact ? (hn[0] > hn[1] ? hn[0] : hn[1]) : nch;
     // this wave's loads of its half's chunk from virtual rank j0 (HR rows, split
     // over the wave pair: 1 KiB blocks HB*wp .. +HB-1 of RPB rows), into buf
@@ -740,14 +743,14 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
     // make E(c) visible, start the next chunk's loads, multiply.  Compact
     // layout: start the next chunk's loads, multiply, make E(c+1) visible.
     auto step = [&](uint8_t* eb, uint8_t* en, int c) {
-        // (one chunk() call for both layouts: the accumulators stay on one path)
-        const uint8_t* ec;
-        int jc, nkk;
+        // (one chunk() call for both layouts: the accumulators stay on one path;
+        // its E buffer is eb plus an offset, so the compiler still sees which
+        // LDS DMA it depends on and need not wait for the next step's)
+        const uint8_t* ec = eb + (compact ? wqu * 16384 : 0);
+        const int jc = compact ? own_lo + HR * c : vlo + 64 * c;
+        const int nkk = compact ? (c < own_n ? HR / 16 : 0) : 4;
         if (compact) {
-            if (c + 1 < own_n) issue_half(en + wq * 16384, own_lo + HR * (c + 1));
-            ec = eb + wq * 16384;
-            jc = own_lo + HR * c;
-            nkk = c < own_n ? HR / 16 : 0;
+            if (c + 1 < own_n) issue_half(en + wqu * 16384, own_lo + HR * (c + 1));
         } else {
             const int j0 = vlo + 64 * c;
             lds_barrier();  // every wave is done with chunk c-1 (its F tiles and the buffer en)
@@ -760,9 +763,6 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
             }
             lds_barrier();
             if (c + 1 < nch) gather(j0 + 64);
-            ec = eb;
-            jc = j0;
-            nkk = 4;
         }
         chunk(ec, jc, nkk);
         if (compact) {
@@ -771,7 +771,7 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
     if (compact) {
-        if (own_n > 0) issue_half(e0 + wq * 16384, own_lo);
+        if (own_n > 0) issue_half(e0 + wqu * 16384, own_lo);
         wait_vmcnt<0>();
         lds_barrier();  // step 0 landed; the token table is read before step 1 overwrites it
     } else {
