@@ -565,14 +565,15 @@ def block_cpu_baseline(hp, seg, ranks, alphas, x, dout, per_segment):
                       "forward and backward with all 7 projections' dA/dB; %.1f s" % (per_segment, len(rows), dt)}
 
 
-def write_block_profile(d):
-    """Kernel-time summary of a rocprofv3 --kernel-trace --stats run of the block bench."""
+def write_stats_profile(d, title, name):
+    """Kernel-time summary of a rocprofv3 --kernel-trace --stats run (trace/ under d)
+    into profiles/<name>."""
     import csv
     import glob
     cmds = json.load(open(os.path.join(d, "commands.json")))
     f = glob.glob(os.path.join(d, "trace", "**", "*kernel_stats.csv"), recursive=True)
     rows = list(csv.DictReader(open(f[0])))
-    lines = ["# rocprofv3 kernel statistics, Llama-3-8B decoder block, 32 adapters x 1024 tokens",
+    lines = ["# rocprofv3 kernel statistics, " + title,
              "# command: " + cmds["trace"], "",
              "%6s %12s %12s %7s  %s" % ("calls", "total_ms", "avg_us", "pct", "kernel")]
     for r in rows:
@@ -580,7 +581,7 @@ def write_block_profile(d):
                                                       float(r["AverageNs"]) / 1e3, float(r["Percentage"]),
                                                       r["Name"][:110]))
     txt = "\n".join(lines) + "\n"
-    open(os.path.join(ROOT, "profiles", "kernels_llama3_8b_block_stats.txt"), "w").write(txt)
+    open(os.path.join(ROOT, "profiles", name), "w").write(txt)
     print(txt)
 
 
@@ -636,7 +637,14 @@ def main():
     args = ap.parse_args()
     if args.rocprof_summary:
         if args.block:
-            write_block_profile(args.rocprof_summary)
+            write_stats_profile(args.rocprof_summary, "Llama-3-8B decoder block, 32 adapters x 1024 tokens",
+                                "kernels_llama3_8b_block_stats.txt")
+        elif args.decode:
+            import workloads
+            wl = workloads.config(args.workload)
+            write_stats_profile(args.rocprof_summary, "decode-shaped forward %s (%d adapters, %d tokens, "
+                                "%d -> %d)" % (wl.name, wl.n_adapters, wl.T, wl.d_in, wl.d_out),
+                                "kernels_%s_stats.txt" % wl.name)
         else:
             write_profiles(args.rocprof_summary, args.workload)
         return
