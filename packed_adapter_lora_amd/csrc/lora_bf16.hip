@@ -121,6 +121,8 @@ constexpr int kShStage = kShX + 128 * kShRowB;   // + up to 128 panel rows: 32 K
 __shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
 __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sh3[kShStage];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sh4[kShStage];
 
 
 template <int MAXJT>
@@ -180,21 +182,28 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
         }
     };
     constexpr int kPer = 4 + MAXJT;  // DMA loads per wave per stage
-    // stage kt in cur; stage kt+1 in flight in nxt; refill prv (stage kt-1, done) with stage kt+2
+    // stage kt in cur; stages kt+1 .. kt+3 in flight; refill prv (stage kt-1,
+    // done) with stage kt+4
     auto step = [&](uint8_t* cur, uint8_t* prv, int kt) {
-        wait_vmcnt<kPer>();  // stage kt landed, stage kt+1 may be in flight
-        lds_barrier();       // and every wave is done with stage kt-1
-        issue(prv, kt + 2);
+        wait_vmcnt<3 * kPer>();  // stage kt landed, stages kt+1 .. kt+3 may be in flight
+        lds_barrier();           // and every wave is done with stage kt-1
+        issue(prv, kt + 4);
         compute(cur);
     };
     issue(g_sh0, kt0);
     issue(g_sh1, kt0 + 1);
-    for (int kt = kt0; kt < kt1; kt += 3) {
-        step(g_sh0, g_sh2, kt);
+    issue(g_sh2, kt0 + 2);
+    issue(g_sh3, kt0 + 3);
+    for (int kt = kt0; kt < kt1; kt += 5) {
+        step(g_sh0, g_sh4, kt);
         if (kt + 1 >= kt1) break;
         step(g_sh1, g_sh0, kt + 1);
         if (kt + 2 >= kt1) break;
         step(g_sh2, g_sh1, kt + 2);
+        if (kt + 3 >= kt1) break;
+        step(g_sh3, g_sh2, kt + 3);
+        if (kt + 4 >= kt1) break;
+        step(g_sh4, g_sh3, kt + 4);
     }
     wait_vmcnt<0>();
 
