@@ -73,10 +73,10 @@ def load_traffic(kernel, wl):
     return rec.get("bytes_per_launch")
 
 
-KERNEL_CLASSES = (("gemm_lora_bf16_pipe<true>", "gemm_fwd"), ("gemm_lora_bf16_pipe<false>", "gemm_bwd"),
+KERNEL_CLASSES = (("gemm_lora_bf16_pipe<true", "gemm_fwd"), ("gemm_lora_bf16_pipe<false", "gemm_bwd"),
                   ("gemm_lora_bf16<true>", "gemm_fwd"), ("gemm_lora_bf16<false>", "gemm_bwd"),
-                  ("shrink_bf16", "shrink"), ("wgrad_reduce", "reduce"), ("wgrad_bf16", "wgrad"),
-                  ("adamw_panel", "adamw"))
+                  ("shrink_bf16", "shrink"), ("shrink_slice_sum", "shrink_sum"), ("wgrad_reduce", "reduce"),
+                  ("wgrad_bf16", "wgrad"), ("wgrad_prep", "wgrad_prep"), ("adamw_panel", "adamw"))
 
 
 def kernel_class(name):
@@ -600,7 +600,8 @@ def write_profiles(d, workload):
         open(os.path.join(prof, "kernels_%s_mfma_clock.txt" % wl.name), "w").write(res["mfma_txt"])
         print(res["mfma_txt"])
     src = {"gemm_fwd": "gemm_bf16.hip", "gemm_bwd": "gemm_bf16.hip", "shrink": "lora_bf16.hip",
-           "wgrad": "lora_bf16.hip", "reduce": "lora_bf16.hip", "adamw": "optim.hip"}
+           "shrink_sum": "lora_bf16.hip", "wgrad": "lora_bf16.hip", "wgrad_prep": "lora_bf16.hip",
+           "reduce": "lora_bf16.hip", "adamw": "optim.hip"}
     tj = {}
     for cls, rec in res["traffic"].items():
         f = os.path.join(ROOT, "packed_adapter_lora_amd", "csrc", src[cls])
