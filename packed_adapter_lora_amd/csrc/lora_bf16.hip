@@ -106,35 +106,39 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined shrink (K a multiple of 64): one workgroup per 128-token tile of
-// one adapter, or per K slice of it (shrink_slices: adapters of a few tokens,
-// whose single tile would otherwise walk all of K on one CU).  Each 64-k stage brings the tile's 128 rows of X/dY and the
-// adapter's 32*MAXJT panel rows into LDS with LDS DMA (1 KiB per instruction =
-// 8 rows x 128 B, whole cache lines), three stages deep so two stay in flight;
-// wavefront w multiplies its 32 token rows against the panel.  Rows past the
-// segment, the tensor or the rank read as zero (outside the buffer range).
+// Pipelined shrink (K a multiple of 64): one workgroup of WPG waves per tile
+// of 32*WPG tokens of one adapter, or per K slice of it (shrink_slices:
+// adapters of a few tokens, whose single tile would otherwise walk all of K
+// on one CU).  Each 64-k stage brings the tile's token rows of X/dY and the
+// adapter's 32*MAXJT panel rows into LDS with LDS DMA (1 KiB per instruction
+// = 8 rows x 128 B, whole cache lines), five stages deep so four stay in
+// flight; wavefront w multiplies its 32 token rows against the panel.  Rows
+// past the segment, the tensor or the rank read as zero (outside the buffer
+// range).  A wave's MFMA sequence for its 32 rows is the same for any WPG,
+// so both tile sizes give the same bits: WPG = 4 (128-token tiles) normally,
+// WPG = 1 when the 128-token tiles would leave most CUs idle (a CU's own
+// stream of loads, not its arithmetic, bounds this kernel).
 // ---------------------------------------------------------------------------
 constexpr int kShRowB = 128;                     // bytes per LDS row (64 bf16 of k)
-constexpr int kShX = kShrinkTileRows * kShRowB;  // 16 KiB of token rows per stage
-constexpr int kShStage = kShX + 128 * kShRowB;   // + up to 128 panel rows: 32 KiB
 
-__shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
-__shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
-__shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
-__shared__ __attribute__((aligned(1024))) uint8_t g_sh3[kShStage];
-__shared__ __attribute__((aligned(1024))) uint8_t g_sh4[kShStage];
-
-
-template <int MAXJT>
-__global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
+template <int MAXJT, int WPG>
+__global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
+    constexpr int TR = 32 * WPG;                           // token rows per tile
+    constexpr int kShX = TR * kShRowB;                     // token rows per stage
+    constexpr int kShStage = kShX + 32 * MAXJT * kShRowB;  // + the panel rows
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh3[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh4[kShStage];
     const int unit = (int)blockIdx.x;
     const int64_t K = a.K;
     const int i = adapter_of_unit(m, seg.n, unit);
     const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
     const int nsl = shrink_slices(s1 - s0, seg.rank[i], K, a.scratch_row);
     const int u = unit - m.pre[i], slice = u % nsl;
-    const int64_t t0 = s0 + (int64_t)(u / nsl) * kShrinkTileRows;
-    const int nrows = (int)(s1 - t0 < kShrinkTileRows ? s1 - t0 : kShrinkTileRows);
+    const int64_t t0 = s0 + (int64_t)(u / nsl) * TR;
+    const int nrows = (int)(s1 - t0 < TR ? s1 - t0 : TR);
     const int r = seg.rank[i];
     const int ntj = (r + 31) >> 5;
     const int l = lane_id(), w = wave_id(), l32 = l & 31, lh = l >> 5;
@@ -149,7 +153,9 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
     const uint32_t lane_row = (uint32_t)(r0 * K * 2);
     // this work item's stages: [kt0, kt1) of the K / 64
     const int KT = (int)(K / 64), kt0 = slice * KT / nsl, kt1 = (slice + 1) * KT / nsl;
-    // token tile: blocks 4w .. 4w+3 (16 blocks = 128 rows); panel: blocks MAXJT*w .. (4*MAXJT blocks)
+    // token tile: blocks 4w .. 4w+3 (32 rows per wave); panel: 4*MAXJT blocks,
+    // PB per wave
+    constexpr int PB = 4 * MAXJT / WPG;
     auto issue = [&](uint8_t* buf, int kt) {
         const uint32_t oob = kt < kt1 ? 0u : 0x80000000u;
         const uint32_t kb = (uint32_t)kt * 128u + oob;
@@ -160,8 +166,8 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < MAXJT; ++j) {
-            const int blk = MAXJT * wu + j;
+        for (int j = 0; j < PB; ++j) {
+            const int blk = PB * wu + j;
             const uint32_t vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (8u * K * 2) + kb;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + kShX + blk * 1024), 16, vo, 0, 0, 0);
         }
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
             }
         }
     };
-    constexpr int kPer = 4 + MAXJT;  // DMA loads per wave per stage
+    constexpr int kPer = 4 + PB;  // DMA loads per wave per stage
     // stage kt in cur; stages kt+1 .. kt+3 in flight; refill prv (stage kt-1,
     // done) with stage kt+4
     auto step = [&](uint8_t* cur, uint8_t* prv, int kt) {
@@ -211,9 +217,10 @@ __global__ __launch_bounds__(256, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTabl
     // K slices: slice s of the adapter's [n_i][r_i] block goes to its own rows of
     // the scratch activation, s * n_i * r_i floats in (shrink_slice_sum adds them)
     float* __restrict__ out =
-        nsl == 1 ? a.out + seg.hoff[i] + (t0 - s0) * r
-                 : reinterpret_cast<float*>(static_cast<uint8_t*>(a.scratch) + s0 * a.scratch_row) +
-                       (int64_t)slice * (s1 - s0) * r;
+        (nsl == 1 ? a.out + seg.hoff[i]
+                  : reinterpret_cast<float*>(static_cast<uint8_t*>(a.scratch) + s0 * a.scratch_row) +
+                        (int64_t)slice * (s1 - s0) * r) +
+        (t0 - s0) * r;
 #pragma unroll
     for (int jt = 0; jt < MAXJT; ++jt) {
         const int j = jt * 32 + l32;
@@ -587,17 +594,27 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
         (int64_t)s.roff[s.n] * a_in.K * 2 < (int64_t(1) << 31)) {
         ShrinkArgs a = a_in;
         if (!a.scratch) a.scratch_row = 0;
-        WorkMap m128;
+        WorkMap mp;
         bool split = false;
-        const int32_t items = build_shrink_pipe_map(s, &m128, a.K, a.scratch_row, &split);
-        const dim3 grid((unsigned)items), block(256);
-        switch ((s.rmax + 31) / 32) {
-            case 1: hipLaunchKernelGGL(shrink_bf16_pipe<1>, grid, block, 0, st, a, s, m128); break;
-            case 2: hipLaunchKernelGGL(shrink_bf16_pipe<2>, grid, block, 0, st, a, s, m128); break;
-            case 3: hipLaunchKernelGGL(shrink_bf16_pipe<3>, grid, block, 0, st, a, s, m128); break;
-            default: hipLaunchKernelGGL(shrink_bf16_pipe<4>, grid, block, 0, st, a, s, m128); break;
+        int32_t items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows);
+        // 32-token tiles (one wave each) when the 128-token ones fill at most
+        // half of the CUs: four times the workgroups, same results
+        int dev = 0, cus = 256;
+        if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        const bool small = 2 * (int64_t)items <= cus;
+        if (small) items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, 32);
+        const dim3 grid((unsigned)items), block(small ? 64 : 256);
+        switch (((s.rmax + 31) / 32) * 2 + (small ? 1 : 0)) {
+            case 2: hipLaunchKernelGGL((shrink_bf16_pipe<1, 4>), grid, block, 0, st, a, s, mp); break;
+            case 3: hipLaunchKernelGGL((shrink_bf16_pipe<1, 1>), grid, block, 0, st, a, s, mp); break;
+            case 4: hipLaunchKernelGGL((shrink_bf16_pipe<2, 4>), grid, block, 0, st, a, s, mp); break;
+            case 5: hipLaunchKernelGGL((shrink_bf16_pipe<2, 1>), grid, block, 0, st, a, s, mp); break;
+            case 6: hipLaunchKernelGGL((shrink_bf16_pipe<3, 4>), grid, block, 0, st, a, s, mp); break;
+            case 7: hipLaunchKernelGGL((shrink_bf16_pipe<3, 1>), grid, block, 0, st, a, s, mp); break;
+            case 8: hipLaunchKernelGGL((shrink_bf16_pipe<4, 4>), grid, block, 0, st, a, s, mp); break;
+            default: hipLaunchKernelGGL((shrink_bf16_pipe<4, 1>), grid, block, 0, st, a, s, mp); break;
         }
-        if (split) hipLaunchKernelGGL(shrink_slice_sum, dim3((unsigned)s.n), block, 0, st, a, s);
+        if (split) hipLaunchKernelGGL(shrink_slice_sum, dim3((unsigned)s.n), dim3(256), 0, st, a, s);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);

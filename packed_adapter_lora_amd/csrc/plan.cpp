@@ -83,7 +83,8 @@ int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows) {
     return t;
 }
 
-int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split) {
+int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split,
+                              int rows) {
     int32_t t = 0;
     *any_split = false;
     for (int i = 0; i < s.n; ++i) {
@@ -91,7 +92,7 @@ int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t 
         const int64_t ni = s.off[i + 1] - s.off[i];
         const int sl = shrink_slices(ni, s.rank[i], K, row_bytes);
         *any_split = *any_split || sl > 1;
-        t += (int32_t)((ni + kShrinkTileRows - 1) / kShrinkTileRows) * sl;
+        t += (int32_t)((ni + rows - 1) / rows) * sl;
     }
     m->pre[s.n] = t;
     return t;

@@ -84,10 +84,11 @@ constexpr int shrink_slices(int64_t n, int r, int64_t K, int64_t row_bytes) {
                : 1;
 }
 
-// Work items of the pipelined shrink: tiles of 128 tokens x shrink_slices()
+// Work items of the pipelined shrink: tiles of `rows` tokens x shrink_slices()
 // per adapter.  Returns the total; *any_split tells whether a partial sum
 // pass is needed.
-int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split);
+int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split,
+                              int rows);
 
 // Token-chunk size of the weight-gradient reduction over a feature width D.
 // It depends only on D, so an adapter's reduction order is the same whether
