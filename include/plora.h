@@ -60,8 +60,10 @@
  * streams race, as any two kernels writing one buffer would.
  *
  * Environment.  PLORA_GEMM_TILE_P=128 or 256 forces the feature width of the
- * bf16 GEMM tiles of plora_forward / plora_backward_dx (by default it is
- * chosen per shape and device).  Results are bitwise the same either way.
+ * bf16 GEMM tiles of plora_forward / plora_backward_dx, and
+ * PLORA_SHRINK_TILE_ROWS=32 or 128 the token rows of their shrink tiles (by
+ * default both are chosen per shape and device).  Results are bitwise the
+ * same either way.
  */
 #ifndef PLORA_H
 #define PLORA_H

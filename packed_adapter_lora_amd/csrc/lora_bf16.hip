@@ -20,6 +20,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <cstdlib>
+
 namespace plora {
 namespace {
 
@@ -601,7 +603,10 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
         // half of the CUs: four times the workgroups, same results
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        const bool small = 2 * (int64_t)items <= cus;
+        // (PLORA_SHRINK_TILE_ROWS=32 or 128 forces the tile size)
+        const char* force = getenv("PLORA_SHRINK_TILE_ROWS");
+        const int fr = force ? atoi(force) : 0;
+        const bool small = fr == 32 || (fr != 128 && 2 * (int64_t)items <= cus);
         if (small) items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, 32);
         const dim3 grid((unsigned)items), block(small ? 64 : 256);
         switch (((s.rmax + 31) / 32) * 2 + (small ? 1 : 0)) {

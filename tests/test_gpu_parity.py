@@ -80,6 +80,24 @@ def test_bf16_pipelined_tails_full(P, tile_p, monkeypatch):
     full_case(P, wl)
 
 
+def test_shrink_tile_rows_bitwise_equal(P, monkeypatch):
+    """32- and 128-token shrink tiles give each token row the same MFMA sequence
+    (K slices included): equal bits in H, G and everything after them."""
+    import torch
+    wl = workloads.custom(512, 768, [100, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
+                          [32.0, 16.0, 8.0, 16.0, 4.0, 256.0], "bf16", seed=32, name="shrink_tiles")
+    log("case %s" % wl.name)
+    inp = workloads.make_inputs(wl)
+    dev = device_inputs(wl, inp)
+    out = {}
+    for rows in ("128", "32"):
+        monkeypatch.setenv("PLORA_SHRINK_TILE_ROWS", rows)
+        out[rows] = run_gpu(P, wl, dev)
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    for k in ("H", "G", "Y", "dX", "dA", "dB"):
+        assert torch.equal(bits(out["128"][k]), bits(out["32"][k])), k
+
+
 # (384, 704): pipelined forward with a feature tail at either width (704 % 256,
 # 704 % 128); (712, 640): the same for the backward GEMM (d_in = 712).
 @pytest.mark.parametrize("d_in,d_out", [(384, 704), (712, 640)])
