@@ -376,14 +376,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
     }
 }
 
-// dK, dV: work item = (sequence, key/value head, 64 keys); 8 waves = (32-key
-// block, one of 4 query heads).  Query tiles of 32 rows stream through LDS for
-// 4 query heads at a time (one token's 4 head rows are 1 KiB contiguous):
-// Q, dO, and the rows' lse and delta, double-buffered.  Each wave keeps its
-// keys' K and V rows as MFMA operands in registers and accumulates partial dK
-// and dV for its query head; the 4 partials of a key block are summed through
-// LDS at the end.
+// dK, dV: work item = (sequence, key/value head, 32 keys); 4 waves = the 4
+// query heads of the key/value head.  Query tiles of 32 rows stream through
+// LDS for the 4 heads at a time (one token's 4 head rows are 1 KiB
+// contiguous): Q, dO, and the rows' lse and delta, double-buffered.  The
+// keys' K and V rows sit in LDS for the whole item (in registers they crowd
+// out the fragment prefetches); each wave accumulates partial dK and dV for
+// its query head, and the 4 partials are summed through LDS at the end.
 constexpr int kBwdQRows = 32;
+constexpr int kBwdKTile = 32;                    // keys per dK/dV work item
 constexpr int kBwdRow = 1024;                    // 4 heads x 256 bytes per token
 constexpr int kBwdTile = kBwdQRows * kBwdRow;    // 32 KiB
 __shared__ __attribute__((aligned(1024))) uint8_t g_bq0[kBwdTile];
@@ -392,29 +393,33 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_bd0[kBwdTile];
 __shared__ __attribute__((aligned(1024))) uint8_t g_bd1[kBwdTile];
 __shared__ __attribute__((aligned(16))) float g_bl0[2 * 4 * kBwdQRows];  // lse*log2e rows, then delta rows
 __shared__ __attribute__((aligned(16))) float g_bl1[2 * 4 * kBwdQRows];
+__shared__ __attribute__((aligned(1024))) uint8_t g_bkv[2 * kBwdKTile * 256];  // the keys' K rows, then V rows
 
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTable s) {
+// (4 waves of 512 registers each: the K/V fragments and both accumulators
+// stay in registers, so nothing is spilled inside the query loop)
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTable s) {
     int seq, kt;
     tile_of(s, (int)blockIdx.x, seq, kt, false);  // early key tiles see the most queries: first
     const int l = lane_id(), w = wave_id(), l32 = l & 31, lh = l >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    const int kb = w >> 2, hw = w & 3;
+    const int kb = 0, hw = w;
     const int kvh = (int)blockIdx.y;
     const int grp = a.n_q / a.n_kv, nquads = grp / 4;
     const int64_t t0 = s.off[seq];
     const int len = s.off[seq + 1] - s.off[seq];
-    const int key = kt * kAttnQTile + kb * 32 + l32;  // this lane's key (column of S)
+    const int key = kt * kBwdKTile + kb * 32 + l32;  // this lane's key (column of S)
     const bool kok = key < len;
     const int64_t qstride = (int64_t)a.n_q * kHeadDim, kstride = (int64_t)a.n_kv * kHeadDim;
 
-    bf16x8 kf[8], vf[8];
-    {
-        const int64_t ro = (t0 + (kok ? key : 0)) * kstride + kvh * kHeadDim + 8 * lh;
+    // K and V rows of the 32 keys into g_bkv (swizzled 256-byte rows; keys past
+    // the sequence read as zero): 1024 chunks of 16 bytes, 4 per thread
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            kf[kk] = as_bf16x8(load16_or_zero(static_cast<const bf16*>(a.k) + ro + 16 * kk, kok));
-            vf[kk] = as_bf16x8(load16_or_zero(static_cast<const bf16*>(a.v) + ro + 16 * kk, kok));
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int idx = (int)threadIdx.x + 256 * i, ten = idx >> 9, row = (idx >> 4) & 31, ch = idx & 15;
+        const int kr = kt * kBwdKTile + row;
+        const bf16* src = static_cast<const bf16*>(ten ? a.v : a.k) +
+                          (t0 + (kr < len ? kr : 0)) * kstride + kvh * kHeadDim + 8 * ch;
+        *reinterpret_cast<u32x4*>(g_bkv + ten * (kBwdKTile * 256) + swz256(row, ch)) = load16_or_zero(src, kr < len);
     }
 
     // query rows of this sequence; rows past it read as zero
@@ -426,25 +431,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
         (void*)a.lse, 0, (int)(a.T * a.n_q * 4), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
         (void*)a.delta, 0, (int)(a.T * a.n_q * 4), kRsrcWord3);
-    const int qt0 = (kt * kAttnQTile) / kBwdQRows;      // first query tile that can see these keys
+    const int qt0 = (kt * kBwdKTile) / kBwdQRows;       // first query tile that can see these keys
     const int nqt = (len + kBwdQRows - 1) / kBwdQRows;   // query tiles of the sequence
     const int nst = (nqt - qt0) * nquads;                // stages: (query tile, head quad)
     const int hsh = l >> 4, hpc = l & 15;                // DMA lane: head of the row, physical chunk
     // stage z: query tile qt0 + z / nquads, heads kvh*grp + 4*(z % nquads) + 0..3.
-    // Wave w loads token rows 4w .. 4w+3 of Q and of dO; waves 0..3 also one
-    // of the four lse/delta pieces (4-byte loads: 2 heads x 32 queries each).
+    // Wave w loads token rows 8w .. 8w+7 of Q and of dO, and one of the four
+    // lse/delta pieces (4-byte loads: 2 heads x 32 queries each): 17 loads.
     auto issue = [&](uint8_t* qbuf, uint8_t* dbuf, float* lbuf, int z) {
         const int qt = qt0 + z / nquads;
         const int hq0 = kvh * grp + 4 * (z % nquads);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * wu + j;  // token row of the tile
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * wu + j;  // token row of the tile
             const uint32_t vo = (uint32_t)((int64_t)(qt * kBwdQRows + r) * qstride * 2) +
                                 (uint32_t)((hq0 + hsh) * 256) + (uint32_t)((hpc ^ (r & 15)) << 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qbuf + r * kBwdRow), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dbuf + r * kBwdRow), 16, vo, 0, 0, 0);
         }
-        if (wu < 4) {
+        {
             // piece wu: lse (wu < 2) or delta rows of heads 2*(wu%2) .. +1, 32 queries each
             const int hh = 2 * (wu & 1) + (l >> 5);
             const int64_t e = (int64_t)(hq0 + hh) * a.T + t0 + qt * kBwdQRows + (l & 31);
@@ -462,13 +467,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
 
     auto stage = [&](const uint8_t* qbuf, const uint8_t* dbuf, const float* lbuf, int z) {
         const int qt = qt0 + z / nquads;
-        const uint8_t* qh = qbuf + hw * 256;  // this wave's head within the 1 KiB rows
-        const uint8_t* dh = dbuf + hw * 256;
+        // (an opaque zero in the bases: the fragment addresses are formed per
+        // stage instead of occupying registers across the loop)
+        int oz;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(oz));
+        const uint8_t* qh = qbuf + hw * 256 + oz;  // this wave's head within the 1 KiB rows
+        const uint8_t* dh = dbuf + hw * 256 + oz;
         f32x16 st = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            st = mfma32x32x16(frag_row<kBwdRow>(qh, l32, 2 * kk + lh), kf[kk], st);
-            dp = mfma32x32x16(frag_row<kBwdRow>(dh, l32, 2 * kk + lh), vf[kk], dp);
+            st = mfma32x32x16(frag_row<kBwdRow>(qh, l32, 2 * kk + lh), frag_row(g_bkv, l32, 2 * kk + lh), st);
+            dp = mfma32x32x16(frag_row<kBwdRow>(dh, l32, 2 * kk + lh),
+                              frag_row(g_bkv + kBwdKTile * 256, l32, 2 * kk + lh), dp);
         }
         // lane: key column, query rows 8*(v/4) + 4*lh + v%4 of the tile
 #pragma unroll
@@ -481,7 +491,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
                 const int v = 4 * g4 + e;
                 const int qi = qt * kBwdQRows + r0 + e;
                 const bool vis = kok && qi < len && qi >= key;
-                const float p = vis ? exp2f(st[v] * c - ls[e] * kLog2e) : 0.0f;
+                const float ex = exp2f(st[v] * c - ls[e] * kLog2e);
+                const float p = vis ? ex : 0.0f;
                 st[v] = p;
                 dp[v] = p * (dp[v] - dl[e]);  // dS
             }
@@ -494,6 +505,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
             dv[db] = mfma32x32x16(p1, frag_tr<kBwdRow>(dh, db * 32, 16), dv[db]);
             dk[db] = mfma32x32x16(s0, frag_tr<kBwdRow>(qh, db * 32, 0), dk[db]);
             dk[db] = mfma32x32x16(s1, frag_tr<kBwdRow>(qh, db * 32, 16), dk[db]);
+            // (keep the accumulators in AGPRs across stages: otherwise they are
+            // carried in VGPRs and copied in and out around every stage)
+            asm volatile("" : "+a"(dv[db]), "+a"(dk[db]));
         }
     };
 
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
         for (int z = 0; z < nst; z += 2) {
             if (z + 1 < nst) {
                 issue(g_bq1, g_bd1, g_bl1, z + 1);
-                if (wu < 4) wait_vmcnt<9>(); else wait_vmcnt<8>();
+                wait_vmcnt<17>();  // stage z landed (stage z+1 in flight)
             } else {
                 wait_vmcnt<0>();
             }
@@ -512,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
             if (z + 1 >= nst) break;
             if (z + 2 < nst) {
                 issue(g_bq0, g_bd0, g_bl0, z + 2);
-                if (wu < 4) wait_vmcnt<9>(); else wait_vmcnt<8>();
+                wait_vmcnt<17>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -561,7 +575,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
     bf16* DV = static_cast<bf16*>(a.out3);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        const int kr = kt * kAttnQTile + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+        const int kr = kt * kBwdKTile + kb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
         if (kr >= len) continue;
         const int64_t ro = (t0 + kr) * kstride + kvh * kHeadDim + l32;
 #pragma unroll
@@ -595,7 +609,12 @@ hipError_t launch_attention_bwd(const AttnArgs& a, const SeqTable& s0, hipStream
     hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)s.tiles[s.n], (unsigned)(a.n_q / 4)), dim3(512), 0, st, a,
                        s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)s.tiles[s.n], (unsigned)a.n_kv), dim3(512), 0, st, a, s);
+    SeqTable sk = s0;
+    sk.tiles[0] = 0;
+    for (int i = 0; i < sk.n; ++i)
+        sk.tiles[i + 1] = sk.tiles[i] + (sk.off[i + 1] - sk.off[i] + kBwdKTile - 1) / kBwdKTile;
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)sk.tiles[sk.n], (unsigned)a.n_kv), dim3(256), 0, st, a,
+                       sk);
     return hipGetLastError();
 }
 
