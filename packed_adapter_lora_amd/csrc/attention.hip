@@ -505,9 +505,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
             dv[db] = mfma32x32x16(p1, frag_tr<kBwdRow>(dh, db * 32, 16), dv[db]);
             dk[db] = mfma32x32x16(s0, frag_tr<kBwdRow>(qh, db * 32, 0), dk[db]);
             dk[db] = mfma32x32x16(s1, frag_tr<kBwdRow>(qh, db * 32, 16), dk[db]);
-            // (keep the accumulators in AGPRs across stages: otherwise they are
-            // carried in VGPRs and copied in and out around every stage)
-            asm volatile("" : "+a"(dv[db]), "+a"(dk[db]));
         }
     };
 
