@@ -505,64 +505,82 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
 
-    // Per-adapter records of the tile's adapters (in e1 past the token table,
-    // free until the E loads of step 1): lane j of wave 0 takes adapter
-    // i_first + j, writes its E row table entries (virtual rank -> byte
-    // offset, at most 128 per adapter) and its record; the largest rank goes
-    // into the record area too.
+    // The tile's adapter when it is one of rank <= 64 (the common case): its
+    // fields are wave-uniform (scalar loads), its E rows are addressed without
+    // the row table, and the first E rows are in flight with the H loads.
     const int na = i_last - i_first + 1;
-    int64_t* rec_off = reinterpret_cast<int64_t*>(e1 + 4096);  // 64 x 8 B
-    int64_t* rec_hoff = rec_off + 64;                          // 64 x 8 B
-    int* rec_voff = reinterpret_cast<int*>(rec_hoff + 64);     // 64 x 4 B
-    int* rec_rank = rec_voff + 64;
-    float* rec_scale = reinterpret_cast<float*>(rec_rank + 64);
-    int* rec_rmax = reinterpret_cast<int*>(rec_scale + 64);
-    if (wu == 0) {
-        const int i = i_first + l;
-        int r = 0;
-        if (l < na) {
-            const int v0 = seg.voff[i], vn = seg.voff[i + 1] - v0, rb = seg.roff[i];
-            r = seg.rank[i];
-            // (16 entries per iteration: vn and v0 - vlo are multiples of 16)
-            for (int k = 0; k < vn; k += 16) {
-                u32x4 e[4];
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    e[q >> 2][q & 3] = k + q < r ? (uint32_t)((int64_t)(rb + k + q) * Pdim * 2) : 0x80000000u;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(tab)[(v0 - vlo + k) / 4 + q] = e[q];
-            }
-            rec_off[l] = seg.off[i];
-            rec_hoff[l] = seg.hoff[i];
-            rec_voff[l] = v0;
-            rec_rank[l] = r;
-            rec_scale[l] = seg.scale[i];
-        }
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            const int o = __shfl_xor(r, d);
-            r = o > r ? o : r;
-        }
-        if (l == 0) *rec_rmax = r;
-    }
-    lds_barrier();
-    // this thread's token row: its adapter (the last record starting at or
-    // before it), the adapter's virtual rank range, its H row and scale
+    const int r_first = seg.rank[i_first];
+    const bool single = na == 1 && r_first <= 64;
+    const int rb_first = seg.roff[i_first];
+    const uint32_t row_bytes = (uint32_t)(Pdim * 2);
+
+    // this thread's token row: its adapter, the adapter's virtual rank range,
+    // its H row and scale (zero for rows past the last token)
     const int64_t t = q0 + tid;
-    const int rmax = __builtin_amdgcn_readfirstlane(*rec_rmax);
-    int va = 0, rt = 0;
+    int va = 0, rt = 0, rmax = r_first;
     float sc = 0.0f;
     int64_t hbase = 0;
-    if (t <= tlast) {
-        int lo = 0, hi = na;  // rec_off[lo] <= t < rec_off[hi] (or hi == na)
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (rec_off[mid] <= t) lo = mid; else hi = mid;
+    if (single) {
+        if (t <= tlast) {
+            va = vlo;
+            rt = r_first;
+            sc = seg.scale[i_first];
+            hbase = seg.hoff[i_first] + (t - seg.off[i_first]) * rt;
         }
-        va = rec_voff[lo];
-        rt = rec_rank[lo];
-        sc = rec_scale[lo];
-        hbase = rec_hoff[lo] + (t - rec_off[lo]) * rt;
+    } else {
+        // Per-adapter records of the tile's adapters (in e1 past the token
+        // table, free until the E loads of step 1): lane j of wave 0 takes
+        // adapter i_first + j, writes its E row table entries (virtual rank ->
+        // byte offset, at most 128 per adapter) and its record; the largest
+        // rank goes into the record area too.
+        int64_t* rec_off = reinterpret_cast<int64_t*>(e1 + 4096);  // 64 x 8 B
+        int64_t* rec_hoff = rec_off + 64;                          // 64 x 8 B
+        int* rec_voff = reinterpret_cast<int*>(rec_hoff + 64);     // 64 x 4 B
+        int* rec_rank = rec_voff + 64;
+        float* rec_scale = reinterpret_cast<float*>(rec_rank + 64);
+        int* rec_rmax = reinterpret_cast<int*>(rec_scale + 64);
+        if (wu == 0) {
+            const int i = i_first + l;
+            int r = 0;
+            if (l < na) {
+                const int v0 = seg.voff[i], vn = seg.voff[i + 1] - v0, rb = seg.roff[i];
+                r = seg.rank[i];
+                // (16 entries per iteration: vn and v0 - vlo are multiples of 16)
+                for (int k = 0; k < vn; k += 16) {
+                    u32x4 e[4];
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        e[q >> 2][q & 3] = k + q < r ? (uint32_t)((int64_t)(rb + k + q) * Pdim * 2) : 0x80000000u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(tab)[(v0 - vlo + k) / 4 + q] = e[q];
+                }
+                rec_off[l] = seg.off[i];
+                rec_hoff[l] = seg.hoff[i];
+                rec_voff[l] = v0;
+                rec_rank[l] = r;
+                rec_scale[l] = seg.scale[i];
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                const int o = __shfl_xor(r, d);
+                r = o > r ? o : r;
+            }
+            if (l == 0) *rec_rmax = r;
+        }
+        lds_barrier();
+        rmax = __builtin_amdgcn_readfirstlane(*rec_rmax);
+        if (t <= tlast) {
+            // the last record starting at or before t
+            int lo = 0, hi = na;  // rec_off[lo] <= t < rec_off[hi] (or hi == na)
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (rec_off[mid] <= t) lo = mid; else hi = mid;
+            }
+            va = rec_voff[lo];
+            rt = rec_rank[lo];
+            sc = rec_scale[lo];
+            hbase = rec_hoff[lo] + (t - rec_off[lo]) * rt;
+        }
     }
     const bool compact = rmax <= 64;
     const float* hrow = a.F + hbase;
@@ -610,34 +628,64 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
     // 16 zero bytes past the row table (compact: at most 64 x 64 entries = 16 KiB):
     // the F fragment of lanes whose token does not own the k-step's ranks
     const uint8_t* zero16 = tab + 32768 - 16;
-    if (compact) {
-        gather(va);
-        stage_f();
-        if (tid == 0) *reinterpret_cast<u32x4*>(tab + 32768 - 16) = u32x4{0u, 0u, 0u, 0u};
-    }
-    // token table: first virtual rank of each token's adapter and the end of its
-    // 16-rank groups
-    int* ti = reinterpret_cast<int*>(e1);
-    ti[tid] = va;
-    ti[kThreads + tid] = va + ((rt + 15) & ~15);
-    lds_barrier();  // also orders the row table writes before the first E loads
+    if (compact) gather(va);
     // per MFMA lane and token block nt: the range of token wq*128 + nt*32 + l%32
     // (compact layout); per block: the range of its adapters (tokens are sorted
-    // by adapter: first token's start to last token's end)
+    // by adapter: first token's start to last token's end).  Per 128-token half
+    // (compact layout): its virtual rank range (its first block's start to its
+    // last valid block's end), as HR-rank chunks.
+    constexpr int HR = 16384 / PR::kBytes;  // 32 or 64 rows: 16 KiB per half
     int tva[4], tve[4], blo[4], bhi[4];
+    int hlo[2], hn[2];
+    if (single) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int row = wq * 128 + nt * 32 + l32;
-        tva[nt] = ti[row];
-        tve[nt] = ti[kThreads + row];
-        const int64_t b0 = q0 + (wu >> 1) * 128 + nt * 32;
-        if (b0 > tlast) {
-            blo[nt] = 1;
-            bhi[nt] = 0;
-        } else {
-            const int f = (int)(b0 - q0), e = (int)((b0 + 31 < tlast ? b0 + 31 : tlast) - q0);
-            blo[nt] = __builtin_amdgcn_readfirstlane(ti[f]);  // (wave-uniform: scalar tests below)
-            bhi[nt] = __builtin_amdgcn_readfirstlane(ti[kThreads + e]);
+        for (int nt = 0; nt < 4; ++nt) {
+            const bool in = q0 + wq * 128 + nt * 32 + l32 <= tlast;
+            tva[nt] = in ? vlo : 0;
+            tve[nt] = in ? vhi : 0;
+            const bool bin = q0 + (wu >> 1) * 128 + nt * 32 <= tlast;
+            blo[nt] = bin ? vlo : 1;
+            bhi[nt] = bin ? vhi : 0;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool hin = q0 + h * 128 <= tlast;
+            hlo[h] = hin ? vlo : 0;
+            hn[h] = hin ? (vhi - vlo + HR - 1) / HR : 0;
+        }
+    } else {
+        // token table: first virtual rank of each token's adapter and the end of
+        // its 16-rank groups
+        int* ti = reinterpret_cast<int*>(e1);
+        ti[tid] = va;
+        ti[kThreads + tid] = va + ((rt + 15) & ~15);
+        lds_barrier();  // also orders the row table writes before the first E loads
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int row = wq * 128 + nt * 32 + l32;
+            tva[nt] = ti[row];
+            tve[nt] = ti[kThreads + row];
+            const int64_t b0 = q0 + (wu >> 1) * 128 + nt * 32;
+            if (b0 > tlast) {
+                blo[nt] = 1;
+                bhi[nt] = 0;
+            } else {
+                const int f = (int)(b0 - q0), e = (int)((b0 + 31 < tlast ? b0 + 31 : tlast) - q0);
+                blo[nt] = __builtin_amdgcn_readfirstlane(ti[f]);  // (wave-uniform: scalar tests below)
+                bhi[nt] = __builtin_amdgcn_readfirstlane(ti[kThreads + e]);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t b0 = q0 + h * 128;
+            if (b0 > tlast) {
+                hlo[h] = 0;
+                hn[h] = 0;
+            } else {
+                const int f = h * 128, e = (int)((b0 + 127 < tlast ? b0 + 127 : tlast) - q0);
+                hlo[h] = __builtin_amdgcn_readfirstlane(ti[f]);
+                hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + HR - 1) / HR;
+            }
         }
     }
     // k-steps in pairs: both steps' fragments are read before the first
@@ -698,23 +746,6 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
             }
         }
     };
-    // compact layout: this half's virtual rank range (its first block's start to
-    // its last valid block's end), HR-rank chunks of it, and the step count
-    // (the larger half's chunk count, so every wave takes every barrier)
-    constexpr int HR = 16384 / PR::kBytes;  // 32 or 64 rows: 16 KiB per half
-    int hlo[2], hn[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t b0 = q0 + h * 128;
-        if (b0 > tlast) {
-            hlo[h] = 0;
-            hn[h] = 0;
-        } else {
-            const int f = h * 128, e = (int)((b0 + 127 < tlast ? b0 + 127 : tlast) - q0);
-            hlo[h] = __builtin_amdgcn_readfirstlane(ti[f]);
-            hn[h] = (__builtin_amdgcn_readfirstlane(ti[kThreads + e]) - hlo[h] + HR - 1) / HR;
-        }
-    }
     const int wqu = wu >> 1;  // (this wave's half, wave-uniform)
     const int own_lo = wqu ? hlo[1] : hlo[0], own_n = wqu ? hn[1] : hn[0];
     const int nstep = compact ? (hn[0] > hn[1] ? hn[0] : hn[1]) : nch;
@@ -723,14 +754,20 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
     // (16 KiB)
     const int own_hi = own_lo + HR * own_n;
     constexpr int HB = 8;
-    // (all table reads first, then the loads; rows past the range read zero)
+    // (all row offsets first, then the loads; rows past the range or the
+    // adapter's rank read zero)
     auto issue_half = [&](uint8_t* buf, int j0) {
         uint32_t ro[HB];
 #pragma unroll
         for (int j = 0; j < HB; ++j) {
             const int v = j0 + RPB * (HB * wp + j);
             const bool in = v < own_hi && v < vhi;
-            ro[j] = in ? (uint32_t)rowtab[(in ? v : vlo) + tr - vlo] : 0x80000000u;
+            if (single) {
+                const int k = v + tr - vlo;
+                ro[j] = in && k < r_first ? (uint32_t)(rb_first + k) * row_bytes : 0x80000000u;
+            } else {
+                ro[j] = in ? (uint32_t)rowtab[(in ? v : vlo) + tr - vlo] : 0x80000000u;
+            }
         }
 #pragma unroll
         for (int j = 0; j < HB; ++j) {
@@ -771,9 +808,12 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
         }
     };
     if (compact) {
+        // E of step 0 in flight while F is staged (its H rows were loaded first)
         if (own_n > 0) issue_half(e0 + wqu * 16384, own_lo);
+        stage_f();
+        if (tid == 0) *reinterpret_cast<u32x4*>(tab + 32768 - 16) = u32x4{0u, 0u, 0u, 0u};
         wait_vmcnt<0>();
-        lds_barrier();  // step 0 landed; the token table is read before step 1 overwrites it
+        lds_barrier();  // step 0 and F landed; the token table is read before step 1 overwrites it
     } else {
         issue_e(e0, vlo);
         gather(vlo);
