@@ -137,44 +137,58 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
     f32x16 o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    float m = kNegInf, lsum = 0.0f;
+    // Online softmax with a lazily moved reference: p = 2^(c s - mref), where
+    // mref (shared by the two lanes of a query) only moves when some query of
+    // the wave sees a score more than 2^8 above it; o and the lane's part of
+    // the denominator are rescaled then.  In between, p <= 2^8.
+    float mref = kNegInf, lpart = 0.0f;
     const float c = a.scale * kLog2e;
 
-    // one 64-key tile from LDS, as two halves of 32 keys
+    // one 64-key tile from LDS, as two halves of 32 keys: both score blocks
+    // first, so the second one's products run during the first one's softmax
     auto tile = [&](const uint8_t* kb, const uint8_t* vb, int kt) {
-        const bool diag = kt == qt;
+        f32x16 st[2];
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
-            f32x16 st = f32x16{};
+            st[hb] = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) st = mfma32x32x16(frag_row(kb, hb * 32 + l32, 2 * kk + lh), qf[kk], st);
-            float mx = kNegInf;
+            for (int kk = 0; kk < 8; ++kk)
+                st[hb] = mfma32x32x16(frag_row(kb, hb * 32 + l32, 2 * kk + lh), qf[kk], st[hb]);
+        }
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = kt * kAttnKTile + hb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                float x = st[v] * c;
-                if ((diag && key > qi) || key >= len) x = kNegInf;
-                st[v] = x;
-                mx = fmaxf(mx, x);
+        for (int hb = 0; hb < 2; ++hb) {
+            // causal mask on the diagonal tile: key hb*32 + 8*(v/4) + 4*lh + v%4
+            // of the tile against the query (keys past the sequence only occur
+            // there, after every valid query)
+            if (kt == qt) {
+                const int lim = qi - kt * kAttnKTile - hb * 32 - 4 * lh;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (8 * (v >> 2) + (v & 3) > lim) st[hb][v] = kNegInf;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
-            // a row with no visible key yet keeps mn = -inf: shift by 0 instead
-            const float sh = mn == kNegInf ? 0.0f : mn;
-            const float alpha = exp2f(m - sh);
+            float mx = st[hb][0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, st[hb][v]);
+            const float mxs = mx * c;
+            if (__ballot(mxs > mref + 8.0f)) {
+                const float mn = fmaxf(mref, fmaxf(mxs, __shfl_xor(mxs, 32)));
+                // (a query with no visible key yet keeps -inf; its o and lpart are 0)
+                const float alpha = mn == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(mref - mn);
+                lpart *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db) o[db] *= alpha;
+                mref = mn;
+            }
+            const float sh = mref == kNegInf ? 0.0f : mref;
             float ps = 0.0f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(st[v] - sh);
-                st[v] = p;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[hb][v], c, -sh));
+                st[hb][v] = p;
                 ps += p;
             }
-            ps += __shfl_xor(ps, 32);
-            lsum = lsum * alpha + ps;
-            m = mn;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[db] *= alpha;
-            const bf16x8 p0 = rows_as_b(st, 0), p1 = rows_as_b(st, 1);
+            lpart += ps;
+            const bf16x8 p0 = rows_as_b(st[hb], 0), p1 = rows_as_b(st[hb], 1);
 #pragma unroll
             for (int db = 0; db < 4; ++db) {
                 o[db] = mfma32x32x16(frag_tr(vb, db * 32, hb * 32), p0, o[db]);
@@ -211,6 +225,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
     }
 
     // normalise and store: lane holds query qi, dims db*32 + 8*(v/4) + 4*lh + v%4
+    const float lsum = lpart + __shfl_xor(lpart, 32);
     if (qi < len) {
         const float inv = 1.0f / lsum;
         bf16* row = static_cast<bf16*>(a.out) + (t0 + qi) * qstride + head * kHeadDim;
@@ -224,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
                 *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * g4 + 4 * lh) = v4;
             }
         }
-        if (lh == 0) a.lse[(int64_t)head * a.T + t0 + qi] = (m + log2f(lsum)) / kLog2e;
+        if (lh == 0) a.lse[(int64_t)head * a.T + t0 + qi] = (mref + log2f(lsum)) / kLog2e;
     }
 }
 
@@ -287,7 +302,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
         }
     }
     const float c = a.scale * kLog2e;
-    const float lse2 = qok ? a.lse[(int64_t)head * a.T + t0 + qi] * kLog2e : 0.0f;
+    // (a row past the sequence gets lse = +inf: its p is 0 without a mask)
+    const float lse2 = qok ? a.lse[(int64_t)head * a.T + t0 + qi] * kLog2e : __builtin_inff();
     const float dlt = qok ? a.delta[(int64_t)head * a.T + t0 + qi] : 0.0f;
 
     const uint32_t bytes = (uint32_t)((int64_t)len * kstride * 2);
@@ -321,11 +337,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
                 st = mfma32x32x16(frag_row(kb, hb * 32 + l32, 2 * kk + lh), qf[kk], st);
                 dp = mfma32x32x16(frag_row(vb, hb * 32 + l32, 2 * kk + lh), df[kk], dp);
             }
+            // causal mask on the diagonal tile: key hb*32 + 8*(v/4) + 4*lh + v%4
+            // of the tile against the query (keys past the sequence only occur
+            // there, after every valid query)
+            if (diag) {
+                const int lim = qi - kt * kAttnKTile - hb * 32 - 4 * lh;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (8 * (v >> 2) + (v & 3) > lim) st[v] = kNegInf;
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int key = kt * kAttnKTile + hb * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                const bool vis = qok && key < len && !(diag && key > qi);
-                const float p = vis ? exp2f(st[v] * c - lse2) : 0.0f;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], c, -lse2));
                 st[v] = p * (dp[v] - dlt);  // dS^T
             }
             const bf16x8 s0 = rows_as_b(st, 0), s1 = rows_as_b(st, 1);
@@ -408,7 +431,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
     const int64_t t0 = s.off[seq];
     const int len = s.off[seq + 1] - s.off[seq];
     const int key = kt * kBwdKTile + kb * 32 + l32;  // this lane's key (column of S)
-    const bool kok = key < len;
     const int64_t qstride = (int64_t)a.n_q * kHeadDim, kstride = (int64_t)a.n_kv * kHeadDim;
 
     // K and V rows of the 32 keys into g_bkv (swizzled 256-byte rows; keys past
@@ -480,7 +502,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
             dp = mfma32x32x16(frag_row<kBwdRow>(dh, l32, 2 * kk + lh),
                               frag_row(g_bkv + kBwdKTile * 256, l32, 2 * kk + lh), dp);
         }
-        // lane: key column, query rows 8*(v/4) + 4*lh + v%4 of the tile
+        // lane: key column, query rows 8*(v/4) + 4*lh + v%4 of the tile.  Only
+        // the diagonal tile and the sequence's last tile need a mask: the
+        // causal one, and rows past the sequence (zero Q and dO rows, but the
+        // lse and delta of other tokens).  Keys past the sequence are not stored.
+        if (qt == kt || (qt + 1) * kBwdQRows > len) {
+            const int lim = key - qt * kBwdQRows - 4 * lh, end = len - qt * kBwdQRows - 4 * lh;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 8 * (v >> 2) + (v & 3);
+                if (r < lim || r >= end) st[v] = kNegInf;
+            }
+        }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int r0 = 8 * g4 + 4 * lh;
@@ -489,10 +522,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * g4 + e;
-                const int qi = qt * kBwdQRows + r0 + e;
-                const bool vis = kok && qi < len && qi >= key;
-                const float ex = exp2f(st[v] * c - ls[e] * kLog2e);
-                const float p = vis ? ex : 0.0f;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[v], c, -ls[e] * kLog2e));
                 st[v] = p;
                 dp[v] = p * (dp[v] - dl[e]);  // dS
             }
