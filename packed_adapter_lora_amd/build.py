@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libplora.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "api_block.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip", "optim.hip",
-               "block.hip", "attention.hip"]
+               "block.hip", "attention.hip", "attention_dkv.hip"]
 CXX_SOURCES = ["plan.cpp", "planner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,6 +29,12 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", INCLUDE, "-I", CSRC]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+# Per-source extra flags.  The attention kernels keep their matrix-core
+# accumulators in ordinary VGPRs: left to its heuristics the compiler places
+# the dK/dV accumulators in AGPRs and copies them to and from VGPRs around
+# every query tile.
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "attention_dkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -45,7 +51,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     jobs_list = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
-        jobs_list.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])
+        jobs_list.append([HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(s, []) + ["-c", os.path.join(CSRC, s), "-o", obj])
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
         jobs_list.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])

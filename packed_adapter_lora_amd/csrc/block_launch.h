@@ -12,7 +12,7 @@ constexpr int kRmsMaxChunks = 8;   // RMSNorm rows up to 8 * 256 * 8 = 16384 ele
 constexpr int kHeadDim = 128;      // attention head size
 constexpr int kAttnQTile = 64;     // query rows per attention work item
 constexpr int kAttnKTile = 64;     // keys per attention step (forward and dQ)
-constexpr int kAttnKTileB = 32;    // keys per work item of the dK/dV pass
+constexpr int kAttnKTileB = 64;    // keys per work item of the dK/dV pass
 
 // Sequence table: tokens off[s] .. off[s+1]-1 form sequence s; tiles[s] is the
 // prefix of per-sequence work-item counts (filled per kernel).
@@ -77,5 +77,7 @@ hipError_t launch_swiglu_bwd(const void* da, const void* g, const void* u, void*
 hipError_t launch_add(const void* x, const void* y, void* out, int64_t n, hipStream_t st);
 hipError_t launch_attention_fwd(const AttnArgs& a, const SeqTable& s, hipStream_t st);
 hipError_t launch_attention_bwd(const AttnArgs& a, const SeqTable& s, hipStream_t st);
+// (the dK/dV pass alone; part of launch_attention_bwd, after delta)
+hipError_t launch_attention_dkv(const AttnArgs& a, const SeqTable& s, hipStream_t st);
 
 }  // namespace plora
