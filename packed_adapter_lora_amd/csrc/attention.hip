@@ -35,14 +35,14 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_v0[kAttnKTile * 256];
 __shared__ __attribute__((aligned(1024))) uint8_t g_v1[kAttnKTile * 256];
 
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s) {
-    int seq, qt;
-    tile_of(s, (int)blockIdx.x, seq, qt);
+    int seq, qt, hg;
+    if (!work_item(s, a.n_q / 4, true, seq, qt, hg)) return;
     const int l = lane_id(), w = wave_id(), l32 = l & 31, lh = l >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    const int head = 4 * (int)blockIdx.y + (w & 3);
+    const int head = 4 * hg + (w & 3);
     const int qb = w >> 2;  // this wave's 32-query block of the tile
     const int grp = a.n_q / a.n_kv;
-    const int kvh = (4 * (int)blockIdx.y) / grp;
+    const int kvh = (4 * hg) / grp;
     const int64_t t0 = s.off[seq];
     const int len = s.off[seq + 1] - s.off[seq];
     const int qi = qt * kAttnQTile + qb * 32 + l32;  // this lane's query, within the sequence
@@ -222,14 +222,14 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
 // dQ: work item = (sequence, 4 query heads of one key/value head, 64 queries);
 // 8 waves = (query head, 32-query block), key tiles streamed as in the forward.
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTable s) {
-    int seq, qt;
-    tile_of(s, (int)blockIdx.x, seq, qt);
+    int seq, qt, hg;
+    if (!work_item(s, a.n_q / 4, true, seq, qt, hg)) return;
     const int l = lane_id(), w = wave_id(), l32 = l & 31, lh = l >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(w);
-    const int head = 4 * (int)blockIdx.y + (w & 3);
+    const int head = 4 * hg + (w & 3);
     const int qb = w >> 2;
     const int grp = a.n_q / a.n_kv;
-    const int kvh = (4 * (int)blockIdx.y) / grp;
+    const int kvh = (4 * hg) / grp;
     const int64_t t0 = s.off[seq];
     const int len = s.off[seq + 1] - s.off[seq];
     const int qi = qt * kAttnQTile + qb * 32 + l32;
@@ -347,24 +347,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
 
 hipError_t launch_attention_fwd(const AttnArgs& a, const SeqTable& s0, hipStream_t st) {
     SeqTable s = s0;
-    s.tiles[0] = 0;
-    for (int i = 0; i < s.n; ++i) s.tiles[i + 1] = s.tiles[i] + (s.off[i + 1] - s.off[i] + kAttnQTile - 1) / kAttnQTile;
+    const dim3 grid = attention_grid(s, kAttnQTile, a.n_q / 4);
     if (s.tiles[s.n] == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)s.tiles[s.n], (unsigned)(a.n_q / 4)), dim3(512), 0, st, a, s);
+    hipLaunchKernelGGL(attn_fwd_kernel, grid, dim3(512), 0, st, a, s);
     return hipGetLastError();
 }
 
 hipError_t launch_attention_bwd(const AttnArgs& a, const SeqTable& s0, hipStream_t st) {
     SeqTable s = s0;
-    s.tiles[0] = 0;
-    for (int i = 0; i < s.n; ++i) s.tiles[i + 1] = s.tiles[i] + (s.off[i + 1] - s.off[i] + kAttnQTile - 1) / kAttnQTile;
+    const dim3 grid = attention_grid(s, kAttnQTile, a.n_q / 4);
     if (s.tiles[s.n] == 0) return hipSuccess;
     const int64_t lanes = a.T * a.n_q * 16;
     hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)s.tiles[s.n], (unsigned)(a.n_q / 4)), dim3(512), 0, st, a,
-                       s);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(512), 0, st, a, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_attention_dkv(a, s0, st);
 }

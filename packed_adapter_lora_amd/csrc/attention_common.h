@@ -50,10 +50,27 @@ __device__ __forceinline__ bf16x8 rows_as_b(const f32x16& a, int j) {
     return r;
 }
 
-// Work item -> (sequence, tile within it); reverse = 1 walks the tiles from
-// the last (the heaviest query tiles of a causal mask) to the first.
-__device__ __forceinline__ void tile_of(const SeqTable& s, int item, int& seq, int& tile, bool reverse = true) {
-    const int w = reverse ? s.tiles[s.n] - 1 - item : item;
+// Work item -> (sequence, tile within it, head group).  Level order (s.lmax >
+// 0): item (r * n + seq) * ngroups + group is the tile of rank r of its
+// sequence, rank 0 the heaviest (the last tile when last_first, else the
+// first), so equally heavy tiles of all sequences and groups run together and
+// the lightest run last; a sequence with fewer tiles leaves the items of its
+// missing ranks empty (false).  Otherwise blockIdx.x walks the tiles sequence
+// by sequence (each heaviest first) and blockIdx.y is the group.
+__device__ __forceinline__ bool work_item(const SeqTable& s, int ngroups, bool last_first, int& seq, int& tile,
+                                          int& group) {
+    const int item = (int)blockIdx.x;
+    if (s.lmax > 0) {
+        const int per = s.n * ngroups;
+        const int r = item / per, rem = item - r * per;
+        seq = rem / ngroups;
+        group = rem - seq * ngroups;
+        const int nt = s.tiles[seq + 1] - s.tiles[seq];
+        tile = last_first ? nt - 1 - r : r;
+        return r < nt;
+    }
+    group = (int)blockIdx.y;
+    const int w = last_first ? s.tiles[s.n] - 1 - item : item;
     int lo = 0, hi = s.n;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -61,6 +78,27 @@ __device__ __forceinline__ void tile_of(const SeqTable& s, int item, int& seq, i
     }
     seq = lo;
     tile = w - s.tiles[lo];
+    return true;
+}
+
+// Fills s.tiles with ceil(len / per) items per sequence and picks the order:
+// level order unless it would launch more than twice as many (partly empty)
+// items.  Returns the grid.
+inline dim3 attention_grid(SeqTable& s, int per, int ngroups) {
+    s.tiles[0] = 0;
+    int lmax = 0;
+    for (int i = 0; i < s.n; ++i) {
+        const int nt = (s.off[i + 1] - s.off[i] + per - 1) / per;
+        s.tiles[i + 1] = s.tiles[i] + nt;
+        lmax = nt > lmax ? nt : lmax;
+    }
+    const int64_t level_items = (int64_t)lmax * s.n;
+    if (level_items <= 2 * (int64_t)s.tiles[s.n] && level_items * ngroups < (1LL << 31)) {
+        s.lmax = lmax;
+        return dim3((unsigned)(level_items * ngroups), 1);
+    }
+    s.lmax = 0;
+    return dim3((unsigned)s.tiles[s.n], (unsigned)ngroups);
 }
 
 }  // namespace

@@ -41,12 +41,11 @@ __shared__ __attribute__((aligned(16))) float g_tl1[2 * 4 * kDkvQRows];
 __shared__ __attribute__((aligned(1024))) uint8_t g_tk[kDkvKeys * 256];  // the item's K rows
 
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTable s) {
-    int seq, kt;
-    tile_of(s, (int)blockIdx.x, seq, kt, false);  // early key tiles see the most queries: first
+    int seq, kt, kvh;
+    if (!work_item(s, a.n_kv, false, seq, kt, kvh)) return;  // early key tiles see the most queries: first
     const int l = lane_id(), l32 = l & 31, lh = l >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(wave_id());
     const int hw = wu & 3, kb = wu >> 2;  // this wave's head within the quad, key block
-    const int kvh = (int)blockIdx.y;
     const int grp = a.n_q / a.n_kv, nquads = grp / 4;
     const int64_t t0 = s.off[seq];
     const int len = s.off[seq + 1] - s.off[seq];
@@ -249,10 +248,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
 
 hipError_t launch_attention_dkv(const AttnArgs& a, const SeqTable& s0, hipStream_t st) {
     SeqTable s = s0;
-    s.tiles[0] = 0;
-    for (int i = 0; i < s.n; ++i) s.tiles[i + 1] = s.tiles[i] + (s.off[i + 1] - s.off[i] + kDkvKeys - 1) / kDkvKeys;
+    const dim3 grid = attention_grid(s, kDkvKeys, a.n_kv);
     if (s.tiles[s.n] == 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel, dim3((unsigned)s.tiles[s.n], (unsigned)a.n_kv), dim3(512), 0, st, a, s);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel, grid, dim3(512), 0, st, a, s);
     return hipGetLastError();
 }
 

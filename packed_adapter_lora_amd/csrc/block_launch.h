@@ -15,9 +15,11 @@ constexpr int kAttnKTile = 64;     // keys per attention step (forward and dQ)
 constexpr int kAttnKTileB = 64;    // keys per work item of the dK/dV pass
 
 // Sequence table: tokens off[s] .. off[s+1]-1 form sequence s; tiles[s] is the
-// prefix of per-sequence work-item counts (filled per kernel).
+// prefix of per-sequence work-item counts (filled per kernel); lmax > 0 (the
+// most items of one sequence) selects the attention kernels' level order.
 struct SeqTable {
     int32_t n;
+    int32_t lmax;
     int32_t off[kMaxSeq + 1];
     int32_t tiles[kMaxSeq + 1];
 };
