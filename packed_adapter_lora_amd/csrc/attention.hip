@@ -168,23 +168,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
         lds_barrier();
     }
 
-    // normalise and store: lane holds query qi, dims db*32 + 8*(v/4) + 4*lh + v%4
+    // normalise and store (the K/V buffers are free: 8 KiB per wave); lane
+    // holds query qi, dims db*32 + 8*(v/4) + 4*lh + v%4
     const float lsum = lpart + __shfl_xor(lpart, 32);
-    if (qi < len) {
-        const float inv = 1.0f / lsum;
-        bf16* row = static_cast<bf16*>(a.out) + (t0 + qi) * qstride + head * kHeadDim;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[db][4 * g4 + e] * inv);
-                *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * g4 + 4 * lh) = v4;
-            }
-        }
-        if (lh == 0) a.lse[(int64_t)head * a.T + t0 + qi] = (mref + log2f(lsum)) / kLog2e;
-    }
+    const int q0b = qt * kAttnQTile + qb * 32;  // this wave's first query
+    store_rows_via_lds(o, 1.0f / lsum, (wu < 2 ? g_k0 : wu < 4 ? g_k1 : wu < 6 ? g_v0 : g_v1) + (wu & 1) * 8192,
+                       static_cast<bf16*>(a.out) + (t0 + q0b) * qstride + head * kHeadDim, qstride, len - q0b);
+    if (qi < len && lh == 0) a.lse[(int64_t)head * a.T + t0 + qi] = (mref + log2f(lsum)) / kLog2e;
 }
 
 // ===========================================================================
@@ -328,19 +318,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
         lds_barrier();
     }
 
-    if (qok) {
-        bf16* row = static_cast<bf16*>(a.out) + (t0 + qi) * qstride + head * kHeadDim;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                bf16x4 v4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v4[e] = to_bf16(dq[db][4 * g4 + e] * a.scale);
-                *reinterpret_cast<bf16x4*>(row + db * 32 + 8 * g4 + 4 * lh) = v4;
-            }
-        }
-    }
+    // (the K/V buffers are free: 8 KiB per wave)
+    const int q0b = qt * kAttnQTile + qb * 32;  // this wave's first query
+    store_rows_via_lds(dq, a.scale, (wu < 2 ? g_k0 : wu < 4 ? g_k1 : wu < 6 ? g_v0 : g_v1) + (wu & 1) * 8192,
+                       static_cast<bf16*>(a.out) + (t0 + q0b) * qstride + head * kHeadDim, qstride, len - q0b);
 }
 
 }  // namespace

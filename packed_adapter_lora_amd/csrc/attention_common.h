@@ -50,6 +50,31 @@ __device__ __forceinline__ bf16x8 rows_as_b(const f32x16& a, int j) {
     return r;
 }
 
+// Stores a wave's 32 x 128 block of o (lane: row l%32, columns db*32 +
+// 8*(v/4) + 4*(l/32) + v%4 in o[db][v]) times mul as bf16 rows: the lane's
+// values go through the wave's own 8 KiB of LDS (swizzled 256-byte rows),
+// then each store writes 16 bytes per lane, 16 lanes per 256-byte row.  Row r
+// goes to base + r * row_stride (elements) when r < nrows.
+__device__ __forceinline__ void store_rows_via_lds(const f32x16 (&o)[4], float mul, uint8_t* tile, bf16* base,
+                                                   int64_t row_stride, int nrows) {
+    const int l = lane_id(), l32 = l & 31, lh = l >> 5;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = to_bf16(o[db][4 * g4 + e] * mul);
+            *reinterpret_cast<bf16x4*>(tile + swz256(l32, 4 * db + g4) + 8 * lh) = v4;
+        }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (l >> 4), c = l & 15;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(tile + swz256(r, c));
+        if (r < nrows) *reinterpret_cast<u32x4*>(base + r * row_stride + 8 * c) = x;
+    }
+}
+
 // Work item -> (sequence, tile within it, head group).  Level order (s.lmax >
 // 0): item (r * n + seq) * ngroups + group is the tile of rank r of its
 // sequence, rank 0 the heaviest (the last tile when last_first, else the
