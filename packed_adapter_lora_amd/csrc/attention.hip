@@ -31,8 +31,10 @@ namespace {
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_k0[kAttnKTile * 256];
 __shared__ __attribute__((aligned(1024))) uint8_t g_k1[kAttnKTile * 256];
+__shared__ __attribute__((aligned(1024))) uint8_t g_k2[kAttnKTile * 256];
 __shared__ __attribute__((aligned(1024))) uint8_t g_v0[kAttnKTile * 256];
 __shared__ __attribute__((aligned(1024))) uint8_t g_v1[kAttnKTile * 256];
+__shared__ __attribute__((aligned(1024))) uint8_t g_v2[kAttnKTile * 256];
 
 __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s) {
     int seq, qt, hg;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
             const int b = 2 * wu + j;
             const int r = 4 * b + rr;
             const uint32_t vo = (uint32_t)((int64_t)(kt * kAttnKTile + r) * kstride * 2) +
-                                (uint32_t)((pc ^ (r & 15)) << 4);
+                                (uint32_t)((pc ^ rowkey(r)) << 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kb + b * 1024), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vb + b * 1024), 16, vo, 0, 0, 0);
         }
@@ -141,32 +143,28 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
         }
     };
 
-    // causal: key tiles 0 .. qt.  Tile kt+1 is in flight while tile kt is
-    // used; each wave waits for its own loads, then the barrier makes every
-    // wave's loads visible (no vmcnt drain at the barrier).
+    // causal: key tiles 0 .. qt.  Each wave waits for its own loads, then the
+    // barrier makes every wave's loads visible (no vmcnt drain at the barrier).
     const int nkt = qt + 1;
+    // three buffers: tiles kt+1 and kt+2 in flight while tile kt is used; one
+    // barrier per tile (after it, every wave's loads of tile kt are visible
+    // and every wave is done with tile kt-1, whose buffer receives kt+2)
+    auto step = [&](uint8_t* kb, uint8_t* vb, uint8_t* kn, uint8_t* vn, int kt) {
+        if (kt + 1 < nkt) wait_vmcnt<4>(); else wait_vmcnt<0>();  // tile kt landed (kt+1 in flight)
+        lds_barrier();
+        if (kt + 2 < nkt) issue(kn, vn, kt + 2);
+        tile(kb, vb, kt);
+    };
     issue(g_k0, g_v0, 0);
-    for (int kt = 0; kt < nkt; kt += 2) {
-        if (kt + 1 < nkt) {
-            issue(g_k1, g_v1, kt + 1);
-            wait_vmcnt<4>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        lds_barrier();
-        tile(g_k0, g_v0, kt);
-        lds_barrier();  // every wave is done with buffer 0
+    if (nkt > 1) issue(g_k1, g_v1, 1);
+    for (int kt = 0; kt < nkt; kt += 3) {
+        step(g_k0, g_v0, g_k2, g_v2, kt);
         if (kt + 1 >= nkt) break;
-        if (kt + 2 < nkt) {
-            issue(g_k0, g_v0, kt + 2);
-            wait_vmcnt<4>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        lds_barrier();
-        tile(g_k1, g_v1, kt + 1);
-        lds_barrier();
+        step(g_k1, g_v1, g_k0, g_v0, kt + 1);
+        if (kt + 2 >= nkt) break;
+        step(g_k2, g_v2, g_k1, g_v1, kt + 2);
     }
+    lds_barrier();  // every wave is done with the last tile
 
     // normalise and store (the K/V buffers are free: 8 KiB per wave); lane
     // holds query qi, dims db*32 + 8*(v/4) + 4*lh + v%4
@@ -252,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
             const int b = 2 * wu + j;
             const int r = 4 * b + rr;
             const uint32_t vo = (uint32_t)((int64_t)(kt * kAttnKTile + r) * kstride * 2) +
-                                (uint32_t)((pc ^ (r & 15)) << 4);
+                                (uint32_t)((pc ^ rowkey(r)) << 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kb + b * 1024), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vb + b * 1024), 16, vo, 0, 0, 0);
         }

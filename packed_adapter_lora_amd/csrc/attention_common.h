@@ -12,9 +12,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
 // Tiles of 128-wide bf16 rows (256 bytes) in LDS, `stride` bytes apart; the
-// 16-byte chunk c of row r sits at chunk c ^ (r % 16), so 16 consecutive rows
-// read at one chunk hit distinct banks.
-__device__ __forceinline__ int swz(int r, int c, int stride) { return r * stride + ((c ^ (r & 15)) << 4); }
+// 16-byte chunk c of row r sits at chunk c ^ rowkey(r), rowkey(r) = 4 (r % 4)
+// + (r / 4) % 4.  The LDS serves 256 bytes per cycle from 64 banks, so reads
+// are conflict-free when the 16-byte chunks served together are distinct
+// modulo 256 bytes: 16 consecutive rows at one chunk (row reads: rowkey is a
+// bijection on 16 rows), and 4 rows from a multiple of 4 at 4 chunks from a
+// multiple of 4 (transposed reads: rowkey's high bits follow r % 4).
+__device__ __forceinline__ int rowkey(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r, int c, int stride) { return r * stride + ((c ^ rowkey(r)) << 4); }
 __device__ __forceinline__ int swz256(int r, int c) { return swz(r, c, 256); }
 
 // MFMA operand of row r: dims 16*(c/2) + 8*(c%2) .. +7 (chunk c)

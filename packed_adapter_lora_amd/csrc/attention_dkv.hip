@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * wu + j;  // token row of the tile
             const uint32_t vo = (uint32_t)((int64_t)(qt * kDkvQRows + r) * qstride * 2) +
-                                (uint32_t)((hq0 + hsh) * 256) + (uint32_t)((hpc ^ (r & 15)) << 4);
+                                (uint32_t)((hq0 + hsh) * 256) + (uint32_t)((hpc ^ rowkey(r)) << 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(qbuf + r * kDkvRow), 16, vo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dbuf + r * kDkvRow), 16, vo, 0, 0, 0);
         }
