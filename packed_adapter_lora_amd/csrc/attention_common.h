@@ -111,6 +111,33 @@ __device__ __forceinline__ bool work_item(const SeqTable& s, int ngroups, bool l
     return true;
 }
 
+// Work item -> (sequence, tile, head group) in sequence order with the head
+// groups fastest: item t * ngroups + group is tile t of the sequence-major
+// tile list (first tile first).  Consecutive work items go to different XCDs,
+// so with 8 groups each XCD takes one group (one key/value head) and runs
+// the tiles of one or two sequences at a time: their shared query rows stay
+// in its L2.
+__device__ __forceinline__ void work_item_grouped(const SeqTable& s, int ngroups, int& seq, int& tile, int& group) {
+    const int t = (int)blockIdx.x / ngroups;
+    group = (int)blockIdx.x - t * ngroups;
+    int lo = 0, hi = s.n;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s.tiles[mid] <= t) lo = mid; else hi = mid;
+    }
+    seq = lo;
+    tile = t - s.tiles[lo];
+}
+
+// Fills s.tiles with ceil(len / per) items per sequence for work_item_grouped;
+// returns the grid.
+inline dim3 attention_grid_grouped(SeqTable& s, int per, int ngroups) {
+    s.tiles[0] = 0;
+    for (int i = 0; i < s.n; ++i) s.tiles[i + 1] = s.tiles[i] + (s.off[i + 1] - s.off[i] + per - 1) / per;
+    s.lmax = 0;
+    return dim3((unsigned)((int64_t)s.tiles[s.n] * ngroups), 1);
+}
+
 // Fills s.tiles with ceil(len / per) items per sequence and picks the order:
 // level order unless it would launch more than twice as many (partly empty)
 // items.  Returns the grid.

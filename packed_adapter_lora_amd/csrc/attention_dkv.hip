@@ -7,6 +7,8 @@
 // [LLM+LoRA微调加速技术原理解析 (m.youleyou.com), 深入理解LoRA：基本原理与PEFT实现:
 // the attention layer of the Transformer blocks that LoRA adapts].
 //
+// Work items in sequence order, the key/value heads fastest (one per XCD
+// with 8 of them), so the items sharing a sequence's query rows run together.
 // Work item: (sequence, key/value head, 64 keys); 8 waves = (query head of a
 // head quad, 32-key block), two per SIMD.  Orientation S = Q K^T: a lane owns
 // one key of its block and 16 query rows, so P^T and dS^T feed the dV and dK
@@ -42,7 +44,7 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_tk[kDkvKeys * 256];  // the 
 
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTable s) {
     int seq, kt, kvh;
-    if (!work_item(s, a.n_kv, false, seq, kt, kvh)) return;  // early key tiles see the most queries: first
+    work_item_grouped(s, a.n_kv, seq, kt, kvh);
     const int l = lane_id(), l32 = l & 31, lh = l >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(wave_id());
     const int hw = wu & 3, kb = wu >> 2;  // this wave's head within the quad, key block
@@ -248,7 +250,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
 
 hipError_t launch_attention_dkv(const AttnArgs& a, const SeqTable& s0, hipStream_t st) {
     SeqTable s = s0;
-    const dim3 grid = attention_grid(s, kDkvKeys, a.n_kv);
+    const dim3 grid = attention_grid_grouped(s, kDkvKeys, a.n_kv);
     if (s.tiles[s.n] == 0) return hipSuccess;
     hipLaunchKernelGGL(attn_bwd_dkv_kernel, grid, dim3(512), 0, st, a, s);
     return hipGetLastError();
