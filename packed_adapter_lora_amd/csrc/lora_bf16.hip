@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 // bf16 arrays hi = bf16(v), lo = bf16(v - hi), row j of length pad64(n_i)
 // (zero-padded), so the main kernel can stream it as whole 128-byte lines.
 //
-// wgrad_bf16_pipe: one workgroup per (adapter token chunk, 256 features).
+// wgrad_bf16_pipe: one workgroup per (adapter token chunk, 256 features), the
+// feature tiles fastest so the workgroups running together read whole rows.
 // Each 64-token stage brings the chunk's X/dY rows (64 x 512 B, read
 // transposed: MFMA B = features, K = tokens) and the adapter's hi/lo rank
 // panels (32*MAXJT rows x 128 B each, MFMA A = rank rows) into LDS with LDS
@@ -434,8 +435,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     __shared__ __attribute__((aligned(1024))) uint8_t b1[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t b2[kStage];
     const int64_t D = a.D;
-    const int w = (int)blockIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.y * kWgCols;
+    const int w = (int)blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * kWgCols;  // (feature tiles fastest: a chunk's rows are read whole)
     const int i = adapter_of_unit(plan.chunks, seg.n, w);
     const int u = w - plan.chunks.pre[i];
     const int nchunks = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
@@ -650,7 +651,9 @@ hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradP
 hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, bf16* fhi, bf16* flo,
                                   hipStream_t st) {
     const int64_t tk = p.chunk_tokens;
-    if (s.rmax > 64 || fhi == nullptr || tk * a.D * 2 >= (int64_t(1) << 31)) return launch_wgrad_bf16(a, s, p, st);
+    // (the pipelined grid puts the chunks in y: at most 65535 of them)
+    if (s.rmax > 64 || fhi == nullptr || tk * a.D * 2 >= (int64_t(1) << 31) || p.chunks.pre[s.n] > 65535)
+        return launch_wgrad_bf16(a, s, p, st);
     const int R = s.roff[s.n];
     if (R > 0) {
         int64_t maxnp = 0;
@@ -664,7 +667,7 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
     }
     const int32_t units = p.chunks.pre[s.n];
     if (units <= 0) return hipSuccess;
-    const dim3 grid((unsigned)units, (unsigned)p.col_tiles), block(256);
+    const dim3 grid((unsigned)p.col_tiles, (unsigned)units), block(256);
     if (s.rmax <= 32)
         hipLaunchKernelGGL((wgrad_bf16_pipe<1>), grid, block, 0, st, a, s, p, fhi, flo);
     else
