@@ -148,31 +148,36 @@ __device__ __forceinline__ int64_t position_of(const SeqTable& s, int64_t t) {
     return t - s.off[lo];
 }
 
-// Rotary embedding in place: thread handles 4 pairs (i, i + 64) of one head
-// of one token; inverse = 1 applies the transpose (backward).
+// Rotary embedding in place: thread handles 8 pairs (i, i + 64) of one token
+// in every head (8 threads per token), so each angle's sine and cosine are
+// taken once per token; inverse = 1 applies the transpose (backward).
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over T * heads * 16
-    const int64_t per_tok = (int64_t)a.heads * 16;
-    if (idx >= a.T * per_tok) return;
-    const int64_t t = idx / per_tok;
-    const int rem = (int)(idx - t * per_tok);
-    const int hd = rem >> 4, i0 = (rem & 15) * 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over T * 8
+    if (idx >= a.T * 8) return;
+    const int64_t t = idx >> 3;
+    const int i0 = (int)(idx & 7) * 8;
     const float pos = (float)position_of(a.seq, t);
-    bf16* base = static_cast<bf16*>(a.x) + t * a.heads * 128 + hd * 128;
-    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + i0);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + i0 + 64);
-    bf16x4 olo, ohi;
+    float cs[8], sn[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float sn, cs;
-        sincosf(pos * a.inv_freq[i0 + k], &sn, &cs);
-        if (a.inverse) sn = -sn;
-        const float l = static_cast<float>(lo[k]), h = static_cast<float>(hi[k]);
-        olo[k] = to_bf16(l * cs - h * sn);
-        ohi[k] = to_bf16(h * cs + l * sn);
+    for (int k = 0; k < 8; ++k) {
+        sincosf(pos * a.inv_freq[i0 + k], &sn[k], &cs[k]);
+        if (a.inverse) sn[k] = -sn[k];
     }
-    *reinterpret_cast<bf16x4*>(base + i0) = olo;
-    *reinterpret_cast<bf16x4*>(base + i0 + 64) = ohi;
+    bf16* row = static_cast<bf16*>(a.x) + t * a.heads * 128 + i0;
+#pragma unroll 4
+    for (int hd = 0; hd < a.heads; ++hd) {
+        bf16* base = row + hd * 128;
+        float lo[8], hi[8], olo[8], ohi[8];
+        load8(base, lo);
+        load8(base + 64, hi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            olo[k] = lo[k] * cs[k] - hi[k] * sn[k];
+            ohi[k] = hi[k] * cs[k] + lo[k] * sn[k];
+        }
+        store8(base, olo);
+        store8(base + 64, ohi);
+    }
 }
 
 __device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -234,8 +239,8 @@ hipError_t launch_rmsnorm_bwd(const RmsBwdArgs& a, int64_t T, hipStream_t st) {
 }
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t st) {
-    const int64_t n = a.T * a.heads * 16;
-    if (n <= 0) return hipSuccess;
+    const int64_t n = a.T * 8;
+    if (n <= 0 || a.heads <= 0) return hipSuccess;
     hipLaunchKernelGGL(rope_kernel, dim3(blocks_for(n)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
