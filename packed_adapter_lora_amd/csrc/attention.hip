@@ -178,34 +178,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a, SeqTable s
 // ===========================================================================
 // Backward.  With P = exp(S - lse) (lse from the forward), dV = P^T dO,
 // dP = dO V^T, dS = P * (dP - delta), delta = rowsum(dO * O), dQ = scale dS K,
-// dK = scale dS^T Q.  Three kernels: delta; dQ (the forward's orientation,
-// one work item per query tile, streaming key tiles); dK and dV (the other
-// orientation, S = Q K^T with one key per lane, one work item per 64-key tile
-// of one key/value head, streaming query tiles of all its query heads).
+// dK = scale dS^T Q.  Two kernels: dQ (the forward's orientation, one work
+// item per query tile, streaming key tiles; it also writes delta), then dK
+// and dV (attention_dkv.hip: the other orientation, S = Q K^T with one key
+// per lane, one work item per 64-key tile of one key/value head, streaming
+// query tiles of all its query heads).
 // ===========================================================================
-
-// delta[h][t] = sum_d dO[t][h][d] * O[t][h][d]: 16 lanes per (token, head)
-__global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
-    const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // token * n_q + head
-    const int part = threadIdx.x & 15;
-    const bool ok = item < a.T * a.n_q;
-    float acc = 0.0f;
-    if (ok) {
-        const int64_t off = item * kHeadDim + part * 8;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.dO) + off);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.o) + off);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            acc += __uint_as_float(x[k] << 16) * __uint_as_float(y[k] << 16) +
-                   __uint_as_float(x[k] & 0xffff0000u) * __uint_as_float(y[k] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (ok && part == 0) {
-        const int64_t t = item / a.n_q, h = item - t * a.n_q;
-        a.delta[h * a.T + t] = acc;
-    }
-}
 
 // dQ: work item = (sequence, 4 query heads of one key/value head, 64 queries);
 // 8 waves = (query head, 32-query block), key tiles streamed as in the forward.
@@ -224,19 +202,31 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(AttnArgs a, SeqTabl
     const bool qok = qi < len;
     const int64_t qstride = (int64_t)a.n_q * kHeadDim, kstride = (int64_t)a.n_kv * kHeadDim;
 
+    // this lane's query row of Q and dO as B operands, and delta = rowsum(dO * O)
+    // (the two lanes of a query hold 64 of its dims each; the dK/dV pass reads
+    // delta from here)
     bf16x8 qf[8], df[8];
+    float dlt;
     {
         const int64_t ro = (t0 + (qok ? qi : 0)) * qstride + head * kHeadDim + 8 * lh;
+        float dp = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
             qf[kk] = as_bf16x8(load16_or_zero(static_cast<const bf16*>(a.q) + ro + 16 * kk, qok));
-            df[kk] = as_bf16x8(load16_or_zero(static_cast<const bf16*>(a.dO) + ro + 16 * kk, qok));
+            const u32x4 dv = load16_or_zero(static_cast<const bf16*>(a.dO) + ro + 16 * kk, qok);
+            const u32x4 ov = load16_or_zero(static_cast<const bf16*>(a.o) + ro + 16 * kk, qok);
+            df[kk] = as_bf16x8(dv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dp += __uint_as_float(dv[e] << 16) * __uint_as_float(ov[e] << 16) +
+                      __uint_as_float(dv[e] & 0xffff0000u) * __uint_as_float(ov[e] & 0xffff0000u);
         }
+        dlt = dp + __shfl_xor(dp, 32);
+        if (qok && lh == 0) a.delta[(int64_t)head * a.T + t0 + qi] = dlt;
     }
     const float c = a.scale * kLog2e;
     // (a row past the sequence gets lse = +inf: its p is 0 without a mask)
     const float lse2 = qok ? a.lse[(int64_t)head * a.T + t0 + qi] * kLog2e : __builtin_inff();
-    const float dlt = qok ? a.delta[(int64_t)head * a.T + t0 + qi] : 0.0f;
 
     const uint32_t bytes = (uint32_t)((int64_t)len * kstride * 2);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -336,12 +326,9 @@ hipError_t launch_attention_bwd(const AttnArgs& a, const SeqTable& s0, hipStream
     SeqTable s = s0;
     const dim3 grid = attention_grid(s, kAttnQTile, a.n_q / 4);
     if (s.tiles[s.n] == 0) return hipSuccess;
-    const int64_t lanes = a.T * a.n_q * 16;
-    hipLaunchKernelGGL(attn_delta_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(512), 0, st, a, s);  // (also writes delta)
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, grid, dim3(512), 0, st, a, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_attention_dkv(a, s0, st);
 }
 

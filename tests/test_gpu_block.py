@@ -175,7 +175,8 @@ def test_attention_bwd(P, offs, n_q, n_kv):
         # ... and elementwise against the rounding model: the kernel feeds P and dS
         # to the matrix cores as bf16 (relative 2^-9 each), so an element may be
         # off by 2^-9 * sum |dS| |K| (dq), sum |dS| |Q| (dk), sum P |dO| (dv),
-        # plus its own bf16 rounding; twice that is allowed
+        # plus the fp32 rounding of S, dP and delta (bwd_rounding_bounds) and its
+        # own bf16 rounding; twice that is allowed
         err = np.abs(got - ref)
         lim = 2.0 * (bd + 2.0 ** -9 * np.abs(ref)) + 1e-6
         assert np.all(err <= lim), "%s: %d elements beyond the rounding bound; worst ratio %.2f" % (
@@ -184,7 +185,11 @@ def test_attention_bwd(P, offs, n_q, n_kv):
 
 def bwd_rounding_bounds(q, k, v, dO, o, lse, offs, n_q, n_kv):
     """Per-element size of the bf16 rounding of P and dS in the backward
-    products: 2^-9 * (|dS| @ |K|, |dS|^T @ |Q|, P^T @ |dO|), in fp64."""
+    products: 2^-9 * (|dS| @ |K|, |dS|^T @ |Q|, P^T @ |dO|), plus the fp32
+    rounding of the length-128 dot products behind them (at most
+    gamma_128 ~ 2^-17 of the sum of |terms|): the score (an absolute error in
+    the exponent, so relative in P) and dP - delta (absolute, which matters
+    where dP ~ delta and dS itself is small), in fp64."""
     scale, grp = 1.0 / np.sqrt(128.0), n_q // n_kv
     bq, bk, bv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     for a, b in zip(offs[:-1], offs[1:]):
@@ -197,9 +202,12 @@ def bwd_rounding_bounds(q, k, v, dO, o, lse, offs, n_q, n_kv):
             dOh, Oh = dO[a:b, hs].astype(np.float64), o[a:b, hs].astype(np.float64)
             Pm = np.where(mask, np.exp(Q @ K.T * scale - lse[j, a:b][:, None]), 0.0)
             dS = Pm * (dOh @ V.T - np.sum(dOh * Oh, axis=1, keepdims=True))
-            bq[a:b, hs] += 2.0 ** -9 * scale * np.abs(dS) @ np.abs(K)
-            bk[a:b, gs] += 2.0 ** -9 * scale * np.abs(dS).T @ np.abs(Q)
-            bv[a:b, gs] += 2.0 ** -9 * Pm.T @ np.abs(dOh)
+            es = 2.0 ** -17 * scale * (np.abs(Q) @ np.abs(K).T)
+            ed = 2.0 ** -17 * (np.abs(dOh) @ np.abs(V).T + np.sum(np.abs(dOh * Oh), axis=1, keepdims=True))
+            dS_err = 2.0 ** -9 * np.abs(dS) + Pm * ed + np.abs(dS) * es
+            bq[a:b, hs] += scale * dS_err @ np.abs(K)
+            bk[a:b, gs] += scale * dS_err.T @ np.abs(Q)
+            bv[a:b, gs] += (2.0 ** -9 * Pm + Pm * es).T @ np.abs(dOh)
     return bq, bk, bv
 
 
