@@ -135,7 +135,8 @@ def check_attention_out(got, ref, offs, n_q, name, tol=2e-2, elementwise=True):
 # (the last case has one long and three one-token sequences: its work items
 # run sequence by sequence; the others run in rank order)
 @pytest.mark.parametrize("offs,n_q,n_kv", [([0, 1, 65, 200, 333], 8, 2), ([0, 1024, 2048], 32, 8),
-                                          ([0, 64, 64, 127, 128], 4, 1), ([0, 700, 701, 702, 703], 8, 2)])
+                                          ([0, 100, 230], 16, 2), ([0, 64, 64, 127, 128], 4, 1),
+                                          ([0, 700, 701, 702, 703], 8, 2), ([0, 2500], 8, 2)])
 def test_attention_fwd(P, offs, n_q, n_kv):
     import torch
     log("attention fwd offs=%s n_q=%d n_kv=%d" % (offs, n_q, n_kv))
@@ -152,7 +153,7 @@ def test_attention_fwd(P, offs, n_q, n_kv):
 
 @pytest.mark.parametrize("offs,n_q,n_kv", [([0, 1, 65, 200, 333], 8, 2), ([0, 1024, 2048], 32, 8),
                                           ([0, 100, 230], 16, 2), ([0, 64, 64, 127, 128], 4, 1),
-                                          ([0, 700, 701, 702, 703], 8, 2)])
+                                          ([0, 700, 701, 702, 703], 8, 2), ([0, 2500], 8, 2)])
 def test_attention_bwd(P, offs, n_q, n_kv):
     import torch
     log("attention bwd offs=%s n_q=%d n_kv=%d" % (offs, n_q, n_kv))
