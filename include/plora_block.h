@@ -78,7 +78,9 @@ int plora_attention_fwd(int32_t n_seq, const int64_t* seq_offsets, int32_t n_q, 
 
 /* Causal grouped-query attention backward: from dO (and the forward's q, k,
  * v, o, lse) writes dq, dk, dv (shapes of q, k, v).  `delta` is fp32
- * scratch of n_q * T floats (contents on entry do not matter). */
+ * scratch of n_q * T floats (contents on entry do not matter; it holds
+ * rowsum(dO * o) afterwards).  PLORA_ERR_SHAPE when a sequence's queries
+ * exceed 2 GiB or n_q * T * 4 bytes reach 2 GiB. */
 int plora_attention_bwd(int32_t n_seq, const int64_t* seq_offsets, int32_t n_q, int32_t n_kv, const void* q,
                         const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
                         void* dk, void* dv, float* delta, void* stream);

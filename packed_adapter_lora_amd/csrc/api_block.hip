@@ -200,6 +200,7 @@ int plora_attention_bwd(int32_t n_seq, const int64_t* seq_offsets, int32_t n_q, 
         for (int i = 0; i < n_seq; ++i)
             if ((int64_t)(s.off[i + 1] - s.off[i]) * n_q * kHeadDim * 2 >= (int64_t(1) << 31))
                 return bad_shape("a sequence's queries exceed 2 GiB");
+        if (T * (int64_t)n_q * 4 >= (int64_t(1) << 31)) return bad_shape("lse and delta exceed 2 GiB");
         if (T == 0) return PLORA_OK;
         if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !delta)
             return fail(PLORA_ERR_NULL, "q, k, v, o, lse, dO, dq, dk, dv and delta are required");
