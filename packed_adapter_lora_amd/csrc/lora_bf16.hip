@@ -20,6 +20,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <cstdlib>
 
 namespace plora {
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, W
 // Sum of the K slices of the shrink (fixed order 0, 1, ...) into H / G: one
 // workgroup per adapter; adapters that were not sliced return at once.
 __global__ __launch_bounds__(256) void shrink_slice_sum(ShrinkArgs a, SegTable seg) {
-    const int i = (int)blockIdx.x;
+    const int i = (int)blockIdx.y;
     const int64_t n = seg.off[i + 1] - seg.off[i];
     const int r = seg.rank[i];
     const int nsl = shrink_slices(n, r, a.K, a.scratch_row);
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void shrink_slice_sum(ShrinkArgs a, SegTable s
     const float* __restrict__ part =
         reinterpret_cast<const float*>(static_cast<const uint8_t*>(a.scratch) + seg.off[i] * a.scratch_row);
     float* __restrict__ out = a.out + seg.hoff[i];
-    for (int64_t e = threadIdx.x; e < ne; e += 256) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < ne; e += (int64_t)gridDim.x * 256) {
         float v = part[e];
         for (int sl = 1; sl < nsl; ++sl) v += part[sl * ne + e];
         out[e] = v;
@@ -620,7 +621,12 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
             case 8: hipLaunchKernelGGL((shrink_bf16_pipe<4, 4>), grid, block, 0, st, a, s, mp); break;
             default: hipLaunchKernelGGL((shrink_bf16_pipe<4, 1>), grid, block, 0, st, a, s, mp); break;
         }
-        if (split) hipLaunchKernelGGL(shrink_slice_sum, dim3((unsigned)s.n), dim3(256), 0, st, a, s);
+        if (split) {
+            int64_t ne = 0;  // the largest adapter's n_i * r_i: 1024 values per workgroup (at most 64 per adapter)
+            for (int i = 0; i < s.n; ++i) ne = std::max(ne, (int64_t)(s.off[i + 1] - s.off[i]) * s.rank[i]);
+            const int64_t bx = std::min<int64_t>((ne + 1023) / 1024, 64);
+            hipLaunchKernelGGL(shrink_slice_sum, dim3((unsigned)bx, (unsigned)s.n), dim3(256), 0, st, a, s);
+        }
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((units + 3) / 4)), block(256);
