@@ -425,10 +425,23 @@ def run_block_bench(args):
           "A": {k: tb(v) for k, v in hp["A"].items()}, "B": {k: tb(v) for k, v in hp["B"].items()}}
     blk = DecoderBlock(dp, seg, ranks, alphas, seg, **BLOCK_DIMS)
     xd, dd = tb(x), tb(dout)
+    # per-adapter AdamW on every projection's packed A/B: fp32 masters and
+    # moments; the step writes the bf16 operator copies the next forward uses
+    from packed_adapter_lora_amd.block import PROJ
+    opt = {}
+    for pn in PROJ:
+        PA, PB = dp["A"][pn].float().contiguous(), dp["B"][pn].float().contiguous()
+        opt[pn] = (PA, PB, torch.zeros_like(PA), torch.zeros_like(PA), torch.zeros_like(PB), torch.zeros_like(PB))
+    lr = [1e-4 * (1 + (i % 3)) for i in range(n)]
+    count = [0]
 
     def step():
         blk.forward(xd)
-        blk.backward(dd)
+        _, grads = blk.backward(dd)
+        count[0] += 1
+        cfg = P.AdamwConfig(lr, [count[0]] * n)
+        for pn in PROJ:
+            P.plora_adamw_step(blk.desc[pn], cfg, *opt[pn], *grads[pn], dp["A"][pn], dp["B"][pn])
 
     for _ in range(args.warmup):
         step()
@@ -443,7 +456,7 @@ def run_block_bench(args):
     P.plora_profile_enable(False)
     kern = {}
     for cls in ("gemm_fwd", "gemm_bwd", "shrink", "wgrad", "reduce", "norm", "rope", "swiglu", "add", "attn_fwd",
-                "attn_bwd"):
+                "attn_bwd", "adamw"):
         cnt, ms = P.plora_profile_read(cls)
         if cnt:
             kern[cls] = round(ms / args.steps, 4)
@@ -451,7 +464,7 @@ def run_block_bench(args):
     T = int(seg[-1])
     flops = block_flops(seg, ranks, hp)
     achieved = flops / sec / 1e12
-    out = {"metric": "decoder block fwd+bwd tokens/sec (LoRA on 7 projections, %d adapters)" % n,
+    out = {"metric": "decoder block fwd+bwd+AdamW tokens/sec (LoRA on 7 projections, %d adapters)" % n,
            "value": round(T / sec, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(sec * 1e3, 3), "higher_is_better": True, "dtype": "bf16",
            "data": "synthetic (seeded normal draws; no dataset or checkpoint)",
@@ -562,7 +575,8 @@ def block_cpu_baseline(hp, seg, ranks, alphas, x, dout, per_segment):
     dt = time.perf_counter() - t0
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": "first %d tokens of the first 2 adapters' sequences (%d tokens), full Llama-3-8B block dims, "
-                      "forward and backward with all 7 projections' dA/dB; %.1f s" % (per_segment, len(rows), dt)}
+                      "forward and backward with all 7 projections' dA/dB (the AdamW step, a fixed cost per step "
+                      "whatever the tokens, is not in the host sample); %.1f s" % (per_segment, len(rows), dt)}
 
 
 def write_stats_profile(d, title, name):
