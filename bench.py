@@ -178,6 +178,18 @@ def make_device_inputs(wl):
     return inp, dev
 
 
+def workload_label(wl):
+    """Name of a workload by the model shape it stands for, its sizes and its
+    token mix (uniform: tokens per adapter; otherwise the total)."""
+    family = {"tiny": "tiny_fp32", "qwen_q": "qwen2.5_7b_q_proj", "llama_sq": "llama3_8b_square_proj",
+              "llama_up": "llama3_8b_up_proj", "longtail": "llama3_8b_up_proj_longtail"}.get(wl.name, wl.name)
+    if not wl.n_adapters:
+        return family
+    counts = wl.counts
+    mix = ("x_%d_tokens" % int(counts[0])) if (counts == counts[0]).all() else ("%d_tokens_total" % int(counts.sum()))
+    return "%s_%dx%d_%d_adapters_%s" % (family, wl.d_in, wl.d_out, wl.n_adapters, mix)
+
+
 def run_bench(wl, steps, warmup):
     import torch
     import packed_adapter_lora_amd as P
@@ -732,8 +744,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded normal draws; no dataset or checkpoint)",
-        "config": {"workload": "llama3_8b_%s_%dx%d_%d_adapters_x_%d_tokens" % (
-            wl.name, wl.d_in, wl.d_out, wl.n_adapters, int(wl.counts.max())) if wl.n_adapters else wl.name,
+        "config": {"workload": workload_label(wl),
             "d_in": wl.d_in, "d_out": wl.d_out, "n_adapters": wl.n_adapters, "tokens": wl.T,
             "ranks": sorted(set(wl.ranks.tolist())), "sum_ranks": wl.R},
         "roofline": roof,
