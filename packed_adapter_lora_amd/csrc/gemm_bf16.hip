@@ -460,6 +460,10 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_w1[kPipeTile];
 //  - per chunk (some r_i > 64): the 64 virtual ranks of the chunk for every
 //    token, restaged each chunk from registers gathered during the previous
 //    chunk.
+// A tile of one adapter with r_i <= 64 (every tile of long segments) takes
+// the compact layout with a uniform setup: the adapter's fields are scalar
+// loads, its E rows are addressed without the row table, and the first E
+// step is in flight while F is staged.
 // e0/e1 (E), shi/slo (F hi/lo), tab (virtual rank -> E row table, at most
 // 8192 entries): 32 KiB each, free.  e1 first holds a per-token table.
 template <int NM>
