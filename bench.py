@@ -52,7 +52,14 @@ def step_flops(wl):
 
 
 def source_sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source without its comments and blank lines, so that
+    counters stay attached to the code they were taken on."""
+    import re
+    txt = open(path, encoding="utf-8").read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    txt = re.sub(r"//[^\n]*", "", txt)
+    code = "\n".join(ln.rstrip() for ln in txt.splitlines() if ln.strip())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def load_traffic(kernel, wl):
