@@ -46,7 +46,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // One workgroup per row.  xs = x (+ res, rounded to bf16, written to xs_out);
-// rstd = 1 / sqrt(mean(xs^2) + eps); h = xs * rstd * w.
+// rstd = 1 / sqrt(mean(xs^2) + eps); h = xs * rstd * w.  NC chunks of 2048
+// elements per row (the row stays in registers; fewer chunks, more rows in
+// flight).
+template <int NC>
 __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(RmsFwdArgs a) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
@@ -54,9 +57,9 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(RmsFwdArgs a) {
     const bf16* x = static_cast<const bf16*>(a.x) + row * D;
     const bf16* r = a.res ? static_cast<const bf16*>(a.res) + row * D : nullptr;
     float ss = 0.0f;
-    float v[kRmsMaxChunks][8];
+    float v[NC][8];
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
         if (e < D) {
             load8(x + e, v[c]);
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(RmsFwdArgs a) {
     if (threadIdx.x == 0) a.rstd[row] = rstd;
     const bf16* w = static_cast<const bf16*>(a.w);
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
         if (e < D) {
             float wv[8], o[8];
@@ -88,16 +91,17 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(RmsFwdArgs a) {
 }
 
 // One workgroup per row.  g = (dy0 + dy1 + dy2) * w;
-// dx = dres + rstd * g - x * rstd^3 * mean(g * x).
+// dx = dres + rstd * g - x * rstd^3 * mean(g * x).  NC chunks as above.
+template <int NC>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(RmsBwdArgs a) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const int64_t D = a.D;
     const float rstd = a.rstd[row];
-    float g[kRmsMaxChunks][8], xv[kRmsMaxChunks][8];
+    float g[NC][8], xv[NC][8];
     float sgx = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
         if (e < D) {
             float wv[8], t[8];
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(RmsBwdArgs a) {
     const float m = block_sum(sgx, red) / (float)D;
     const float r3m = rstd * rstd * rstd * m;
 #pragma unroll
-    for (int c = 0; c < kRmsMaxChunks; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int64_t e = ((int64_t)c * 256 + threadIdx.x) * 8;
         if (e < D) {
             float o[8], rv[8];
@@ -224,17 +228,35 @@ __global__ __launch_bounds__(256) void add_kernel(const bf16* x, const bf16* y, 
 
 unsigned blocks_for(int64_t n8) { return (unsigned)((n8 + 255) / 256); }
 
+// chunks of 2048 elements a row needs, rounded up to 1, 2, 4 or 8
+int rms_chunks(int64_t D) {
+    const int64_t c = (D + 2047) / 2048;
+    return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm_fwd(const RmsFwdArgs& a, int64_t T, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_fwd_kernel, dim3((unsigned)T), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)T), block(256);
+    switch (rms_chunks(a.D)) {
+        case 1: hipLaunchKernelGGL(rmsnorm_fwd_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(rmsnorm_fwd_kernel<2>, grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL(rmsnorm_fwd_kernel<4>, grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL(rmsnorm_fwd_kernel<kRmsMaxChunks>, grid, block, 0, st, a); break;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_bwd(const RmsBwdArgs& a, int64_t T, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3((unsigned)T), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)T), block(256);
+    switch (rms_chunks(a.D)) {
+        case 1: hipLaunchKernelGGL(rmsnorm_bwd_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(rmsnorm_bwd_kernel<2>, grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL(rmsnorm_bwd_kernel<4>, grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL(rmsnorm_bwd_kernel<kRmsMaxChunks>, grid, block, 0, st, a); break;
+    }
     return hipGetLastError();
 }
 

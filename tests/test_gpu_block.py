@@ -45,7 +45,7 @@ def rnd(a):
     return workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(np.asarray(a, np.float32))).reshape(np.shape(a))
 
 
-@pytest.mark.parametrize("D", [4096, 328])
+@pytest.mark.parametrize("D", [4096, 328, 6000, 10000])
 def test_rmsnorm_fwd(P, D):
     import torch
     T = 77
@@ -66,9 +66,10 @@ def test_rmsnorm_fwd(P, D):
     check_block(host(h), OB.rmsnorm_fwd(x, w, 1e-5)[0], 1e-2, "h (no residual)")
 
 
-def test_rmsnorm_bwd(P):
+@pytest.mark.parametrize("D", [4096, 328, 10000])
+def test_rmsnorm_bwd(P, D):
     import torch
-    T, D = 65, 4096
+    T = 65
     x, w = bf((T, D), 62, 1), bf((1, D), 62, 2)[0]
     dys = [bf((T, D), 62, 3 + k, 0.1) for k in range(3)]
     dres = bf((T, D), 62, 7, 0.1)
