@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -23,7 +24,7 @@ struct ProfRec {
     hipEvent_t a, b;
 };
 struct Prof {
-    bool on = false;
+    std::atomic<bool> on{false};
     std::vector<ProfRec> recs;
     std::vector<hipEvent_t> pool;
     std::mutex mu;
@@ -35,13 +36,18 @@ hipEvent_t take_event();
 // with a HIP event pair recorded under kernel class `cls`.
 template <class Fn>
 hipError_t timed(const char* cls, hipStream_t st, Fn&& fn) {
-    if (!g_prof.on) return fn();
+    if (!g_prof.on.load(std::memory_order_relaxed)) return fn();
     std::lock_guard<std::mutex> lk(g_prof.mu);
     hipEvent_t a = take_event(), b = take_event();
-    if (a) (void)hipEventRecord(a, st);
+    if (!a || !b) {  // (no events: run untimed, keep what was taken)
+        if (a) g_prof.pool.push_back(a);
+        if (b) g_prof.pool.push_back(b);
+        return fn();
+    }
+    (void)hipEventRecord(a, st);
     const hipError_t e = fn();
-    if (b) (void)hipEventRecord(b, st);
-    if (a && b) g_prof.recs.push_back({cls, a, b});
+    (void)hipEventRecord(b, st);
+    g_prof.recs.push_back({cls, a, b});
     return e;
 }
 

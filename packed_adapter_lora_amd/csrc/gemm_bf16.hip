@@ -29,6 +29,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <cstdlib>
 
 namespace plora {
@@ -995,17 +996,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
 }
 }  // namespace
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; atomic, since
+// calls may come from several host threads at once).
 static int cu_count() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st) {
