@@ -165,6 +165,43 @@ def test_no_adapters(P):
         check_block(host(dX), ref["dX"], TOL[dtype], "dX")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_tokens_dAdB(P, dtype):
+    """T = 0 with adapters: every segment is empty, so dA_i = dB_i = 0 (the sums
+    over S_i are empty); overwrite writes the zeros, accumulate leaves the
+    gradients as they were.  Forward and dX touch nothing."""
+    import torch
+    log("case zero_tokens_dAdB dtype=%s" % dtype)
+    ranks, d_in, d_out = [4, 64, 16], 256, 320
+    d = P.Desc([0, 0, 0, 0], ranks, [1.0, 8.0, 2.0], d_in, d_out, dtype)
+    R = sum(ranks)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    X = torch.empty((0, d_in), dtype=tdt, device="cuda")
+    dY = torch.empty((0, d_out), dtype=tdt, device="cuda")
+    H = torch.empty((0,), dtype=torch.float32, device="cuda")
+    G = torch.empty((0,), dtype=torch.float32, device="cuda")
+    Y = torch.empty((0, d_out), dtype=tdt, device="cuda")
+    W = torch.zeros((d_out, d_in), dtype=tdt, device="cuda")
+    A = torch.zeros((R, d_in), dtype=tdt, device="cuda")
+    B = torch.zeros((R, d_out), dtype=tdt, device="cuda")
+    P.plora_forward(d, X, W, A, B, Y, H)
+    assert P.plora_h_elems(d) == 0
+    ws_bytes = P.plora_workspace_bytes(d)
+    for ws in (None, torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device="cuda")):
+        dA = torch.full((R, d_in), float("nan"), dtype=torch.float32, device="cuda")
+        dB = torch.full((R, d_out), float("nan"), dtype=torch.float32, device="cuda")
+        P.plora_backward_dAdB(d, X, dY, H, G, dA, dB, ws)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dA).item() == 0 and torch.count_nonzero(dB).item() == 0
+        kA = torch.arange(R * d_in, dtype=torch.float32, device="cuda").reshape(R, d_in)
+        kB = torch.arange(R * d_out, dtype=torch.float32, device="cuda").reshape(R, d_out)
+        dA.copy_(kA)
+        dB.copy_(kB)
+        P.plora_backward_dAdB(d, X, dY, H, G, dA, dB, ws, accumulate=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dA, kA) and torch.equal(dB, kB)
+
+
 # ---------------------------------------------------------------------------
 # exact cases
 # ---------------------------------------------------------------------------
