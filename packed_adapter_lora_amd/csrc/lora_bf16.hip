@@ -395,6 +395,9 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 // wgrad_prep writes the fp32 H_i (or G_i) block [n_i][r_i] transposed as two
 // bf16 arrays hi = bf16(v), lo = bf16(v - hi), row j of length pad64(n_i)
 // (zero-padded), so the main kernel can stream it as whole 128-byte lines.
+// One workgroup per (64-token block, adapter): the block's 64 rows of r_i
+// values are contiguous in H, so they are read whole, transposed in LDS, and
+// leave as r_i pieces of 128 bytes per array.
 //
 // wgrad_bf16_pipe: one workgroup per (adapter token chunk, 256 features), the
 // feature tiles fastest so the workgroups running together read whole rows.
@@ -406,22 +409,34 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 // (outside the buffer range or zero padding).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void wgrad_prep(const float* F, bf16* hi, bf16* lo, SegTable seg, WgradPlan plan) {
-    const int g = (int)blockIdx.y;  // global rank row R_off[i] + j
-    int i = 0;
-    while (i + 1 < seg.n && seg.roff[i + 1] <= g) ++i;
-    const int j = g - seg.roff[i];
-    const int r = seg.rank[i];
+    const int i = (int)blockIdx.y;
     const int64_t n = seg.off[i + 1] - seg.off[i];
+    const int64_t u0 = (int64_t)blockIdx.x * 64;
+    if (u0 >= n) return;  // (u0 is a multiple of 64: the block holding token n-1 also writes the padding)
+    const int r = seg.rank[i];  // <= 64 on this path
     const int64_t np = pad64(n);
-    const float* __restrict__ Fi = F + seg.hoff[i];
-    bf16* __restrict__ h = hi + plan.ft_off[i] + (int64_t)j * np;
-    bf16* __restrict__ o = lo + plan.ft_off[i] + (int64_t)j * np;
-    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < np; u += (int64_t)gridDim.x * 256) {
-        const float v = u < n ? Fi[u * r + j] : 0.0f;
-        bf16 hb, lb;
-        split_bf16(v, hb, lb);
-        h[u] = hb;
-        o[u] = lb;
+    __shared__ float tile[64 * 65];  // [token][rank], rows of 65 floats: the column reads below hit 64 banks
+    const float* __restrict__ Fi = F + seg.hoff[i] + u0 * r;
+    const int valid = (int)((n - u0 < 64 ? n - u0 : 64) * r);
+    for (int e = (int)threadIdx.x; e < 64 * r; e += 256) {
+        const int t = e / r, j = e - t * r;
+        tile[t * 65 + j] = e < valid ? Fi[e] : 0.0f;
+    }
+    __syncthreads();
+    // thread task e: rank row j = e / 8, tokens u0 + 8q .. +7 (q = e % 8): 16 bytes per array
+    for (int e = (int)threadIdx.x; e < 8 * r; e += 256) {
+        const int j = e >> 3, q = e & 7;
+        u16x8 h8, l8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            bf16 hb, lb;
+            split_bf16(tile[(8 * q + k) * 65 + j], hb, lb);
+            h8[k] = __builtin_bit_cast(uint16_t, hb);
+            l8[k] = __builtin_bit_cast(uint16_t, lb);
+        }
+        const int64_t o = plan.ft_off[i] + (int64_t)j * np + u0 + 8 * q;
+        *reinterpret_cast<u16x8*>(hi + o) = h8;
+        *reinterpret_cast<u16x8*>(lo + o) = l8;
     }
 }
 
@@ -665,8 +680,9 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
         int64_t maxnp = 0;
         for (int i = 0; i < s.n; ++i) maxnp = maxnp > pad64(s.off[i + 1] - s.off[i]) ? maxnp : pad64(s.off[i + 1] - s.off[i]);
         if (maxnp > 0) {
-            const int64_t bx = (maxnp + 255) / 256 < 64 ? (maxnp + 255) / 256 : 64;
-            hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)bx, (unsigned)R), dim3(256), 0, st, a.F, fhi, flo, s, p);
+            // (hi/lo offsets are multiples of 64 elements and the arrays start 16-byte aligned)
+            hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)(maxnp / 64), (unsigned)s.n), dim3(256), 0, st, a.F, fhi, flo,
+                               s, p);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
