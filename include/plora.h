@@ -197,9 +197,10 @@ int plora_adamw_step(const plora_desc* desc, const plora_adamw_config* cfg, floa
  * invalid descriptor. */
 size_t plora_h_elems(const plora_desc* desc);
 
-/* Bytes of workspace plora_backward_dAdB needs for this descriptor (0 when no
- * adapter's tokens are split across work items).  Returns 0 for an invalid
- * descriptor. */
+/* Bytes of workspace plora_backward_dAdB needs for this descriptor: the fp32
+ * partial sums of adapters whose tokens are split across work items and the
+ * bf16 hi/lo transposes of H and G (bf16 only; 0 for PLORA_F32 and when no
+ * adapter has tokens).  Returns 0 for an invalid descriptor. */
 size_t plora_workspace_bytes(const plora_desc* desc);
 
 /* Validates a descriptor without touching the GPU; returns a plora_status. */
@@ -219,7 +220,8 @@ int plora_version(void);
  * "shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce", "adamw").  After the caller has
  * synchronised the stream, plora_profile_read returns the number of launches
  * and their summed duration in milliseconds for one class.  Profiling is a
- * process-wide switch meant for benchmarks; it is not thread-safe. */
+ * process-wide switch meant for benchmarks: while it is on, the launches of
+ * every thread are recorded, one call at a time under a process-wide lock. */
 int plora_profile_enable(int on);
 int plora_profile_read(const char* kernel_class, int* launches, double* total_ms);
 void plora_profile_reset(void);
