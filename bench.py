@@ -107,12 +107,24 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_
 
     out = {}
     stats = rows(trace_dir, "kernel_stats.csv")
-    lines = ["# rocprofv3 kernel statistics, workload %s" % workload, "# command: " + cmds["trace"], "",
-             "%-16s %6s %12s %12s  %s" % ("class", "calls", "total_ms", "avg_us", "kernel")]
+    # launches of the timed steps only: the last steps / (steps + warmup) of each kernel's launches
+    import re
+    m = re.search(r"--steps (\d+) --warmup (\d+)", cmds["trace"])
+    steps, warm = (int(m.group(1)), int(m.group(2))) if m else (1, 0)
+    per_kernel = {}
+    for r in rows(trace_dir, "kernel_trace.csv"):
+        per_kernel.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = ["# rocprofv3 kernel statistics, workload %s" % workload, "# command: " + cmds["trace"],
+             "# timed_avg_us: mean over the launches of the %d timed steps (the first %d warm-up steps' "
+             "launches left out)" % (steps, warm), "",
+             "%-16s %6s %12s %12s %12s  %s" % ("class", "calls", "total_ms", "avg_us", "timed_avg_us", "kernel")]
     for r in stats:
         cls = kernel_class(r["Name"]) or "-"
-        lines.append("%-16s %6s %12.3f %12.1f  %s" % (cls, r["Calls"], float(r["TotalDurationNs"]) / 1e6,
-                                                       float(r["AverageNs"]) / 1e3, r["Name"][:110]))
+        d = per_kernel.get(r["Name"], [])
+        keep = d[len(d) - len(d) * steps // (steps + warm):] if d else []
+        tavg = "%12.1f" % (sum(keep) / len(keep) / 1e3) if keep else "%12s" % "-"
+        lines.append("%-16s %6s %12.3f %12.1f %s  %s" % (cls, r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+                                                          float(r["AverageNs"]) / 1e3, tavg, r["Name"][:110]))
     out["stats"] = "\n".join(lines) + "\n"
 
     def counter(d, cname):
