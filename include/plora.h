@@ -215,6 +215,11 @@ const char* plora_last_error(void);
 /* PLORA_ABI_VERSION of the loaded library. */
 int plora_version(void);
 
+/* Hash of the sources and compile flags the library was built from (16 hex
+ * digits, or "unstamped" for a build that did not pass one), so a caller can
+ * tell whether a prebuilt library matches the sources beside it. */
+const char* plora_source_hash(void);
+
 /* Kernel timing.  With profiling on, the library records a HIP event pair
  * on the call's stream around every kernel it launches (kernel classes:
  * "shrink", "gemm_fwd", "gemm_bwd", "wgrad", "reduce", "adamw").  After the caller has

@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
-    "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version",
+    "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version", "plora_source_hash",
     "plora_profile_enable", "plora_profile_read", "plora_profile_reset", "LIB_PATH", "PLORA_F32", "PLORA_BF16",
 ]
 
@@ -74,6 +74,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libplora.so is not built (run: python packed_adapter_lora_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
+    # refuse a library built from other sources than the ones beside it
+    from .build import source_hash
+    lib.plora_source_hash.restype, lib.plora_source_hash.argtypes = ctypes.c_char_p, []
+    built, here = lib.plora_source_hash().decode(), source_hash()
+    if built != here:
+        raise ImportError("libplora.so was built from other sources (hash %s, sources %s); rebuild it with "
+                          "python packed_adapter_lora_amd/build.py" % (built, here))
     vp, dp = ctypes.c_void_p, ctypes.POINTER(plora_desc)
     fp = ctypes.c_void_p
     sig = {
@@ -105,6 +112,7 @@ def _load():
         "plora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "plora_last_error": (ctypes.c_char_p, []),
         "plora_version": (ctypes.c_int, []),
+        "plora_source_hash": (ctypes.c_char_p, []),
         "plora_profile_enable": (ctypes.c_int, [ctypes.c_int]),
         "plora_profile_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int),
                                               ctypes.POINTER(ctypes.c_double)]),
@@ -129,12 +137,17 @@ class Desc:
     """Owns the host arrays of a ``plora_desc`` (offsets int64, ranks int32, alphas fp32)."""
 
     def __init__(self, offsets, ranks, alphas, d_in, d_out, dtype="bf16", n_tokens=None):
-        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64)
-        self.ranks = np.ascontiguousarray(ranks, dtype=np.int32)
-        self.alphas = np.ascontiguousarray(alphas, dtype=np.float32)
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.int64).reshape(-1)
+        self.ranks = np.ascontiguousarray(ranks, dtype=np.int32).reshape(-1)
+        self.alphas = np.ascontiguousarray(alphas, dtype=np.float32).reshape(-1)
         n = int(self.ranks.shape[0])
-        if self.offsets.shape[0] < 1:
+        if n == 0 and self.offsets.shape[0] < 1:
             self.offsets = np.zeros(1, np.int64)
+        # the library reads offsets[0..n] and alphas[0..n-1] through raw pointers
+        if self.offsets.shape[0] != n + 1:
+            raise ValueError("%d adapters need %d segment offsets, got %d" % (n, n + 1, self.offsets.shape[0]))
+        if self.alphas.shape[0] != n:
+            raise ValueError("%d adapters need %d alphas, got %d" % (n, n, self.alphas.shape[0]))
         T = int(self.offsets[-1]) if n_tokens is None else int(n_tokens)
         self.dtype = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
         self.c = plora_desc(n, self.dtype, T, int(d_in), int(d_out),
@@ -181,7 +194,7 @@ def _check(rc: int):
 
 
 def _check_tensor(name, t, shape, dtype):
-    """Shape/dtype/layout check of a torch tensor against the descriptor."""
+    """Shape, dtype, layout and device check of a torch tensor against the descriptor."""
     if t is None or isinstance(t, int):
         return
     if tuple(t.shape) != tuple(shape):
@@ -190,6 +203,13 @@ def _check_tensor(name, t, shape, dtype):
         raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    # a host tensor's address handed to a kernel would fault the GPU
+    if not t.is_cuda:
+        raise ValueError("%s is on %s; the operator needs device memory" % (name, t.device))
+    import torch
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s but the current device is cuda:%d" % (name, t.device,
+                                                                          torch.cuda.current_device()))
 
 
 def _elt(desc):
@@ -293,6 +313,10 @@ def plora_last_error() -> str:
 
 def plora_version() -> int:
     return int(_lib.plora_version())
+
+
+def plora_source_hash() -> str:
+    return _lib.plora_source_hash().decode()
 
 
 def plora_profile_enable(on: bool = True):

@@ -7,6 +7,8 @@ compiler otherwise forms v_pk_* fp32 ops from ordinary float code).
 """
 from __future__ import annotations
 
+import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -37,6 +39,26 @@ EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "attention_dkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
+def source_hash() -> str:
+    """16 hex digits over the library's sources, headers and compile flags
+    (paths relative to the repository, so the same tree hashes the same on
+    any machine).  The library carries the hash it was built from
+    (plora_source_hash), and the package refuses a library whose hash differs
+    from the sources beside it."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(INCLUDE, "*.h")))
+    for f in files:
+        if not os.path.isfile(f):
+            continue
+        h.update(os.path.relpath(f, ROOT).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    flags = [x.replace(ROOT, ".") for x in HIP_FLAGS + CXX_FLAGS] + sorted(
+        k + ":" + " ".join(v) for k, v in EXTRA_FLAGS.items())
+    h.update("\0".join(flags).encode())
+    return h.hexdigest()[:16]
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # the host pass of hipcc does not know the packed-fp32 feature; that note is harmless
@@ -48,10 +70,12 @@ def _run(cmd):
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    stamp = ["-DPLORA_SOURCE_HASH=\"%s\"" % source_hash()]
     jobs_list = []
     for s in HIP_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
-        jobs_list.append([HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(s, []) + ["-c", os.path.join(CSRC, s), "-o", obj])
+        extra = EXTRA_FLAGS.get(s, []) + (stamp if s == "api.hip" else [])
+        jobs_list.append([HIPCC] + HIP_FLAGS + extra + ["-c", os.path.join(CSRC, s), "-o", obj])
     for s in CXX_SOURCES:
         obj = os.path.join(BUILD, s + ".o")
         jobs_list.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj])

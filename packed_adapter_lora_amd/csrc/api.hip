@@ -18,6 +18,10 @@
 #include "plan.h"
 #include "plora.h"
 
+#ifndef PLORA_SOURCE_HASH
+#define PLORA_SOURCE_HASH "unstamped"
+#endif
+
 namespace plora {
 
 thread_local std::string g_last_error;
@@ -81,6 +85,8 @@ const char* plora_status_string(int s) {
 const char* plora_last_error(void) { return g_last_error.c_str(); }
 
 int plora_version(void) { return PLORA_ABI_VERSION; }
+
+const char* plora_source_hash(void) { return PLORA_SOURCE_HASH; }
 
 int plora_validate(const plora_desc* d) {
     const char* why = "";

@@ -139,6 +139,40 @@ def test_python_shape_checks(P):
         P.plora_forward(d, X.float(), None, None, None, None, None, stream=0)
 
 
+def test_python_device_checks(P):
+    """Host tensors of the right shape and dtype are refused before the call:
+    their addresses would reach a kernel as device pointers."""
+    torch = pytest.importorskip("torch")
+    d = desc(P, counts=(3, 0, 5), d_in=64, d_out=32)
+    bf = torch.bfloat16
+    X, W = torch.zeros(8, 64, dtype=bf), torch.zeros(32, 64, dtype=bf)
+    A, B = torch.zeros(28, 64, dtype=bf), torch.zeros(28, 32, dtype=bf)
+    Y, H = torch.zeros(8, 32, dtype=bf), torch.zeros(P.plora_h_elems(d), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device memory"):
+        P.plora_forward(d, X, W, A, B, Y, H, stream=0)
+    dX, G = torch.zeros(8, 64, dtype=bf), torch.zeros(P.plora_h_elems(d), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device memory"):
+        P.plora_backward_dx(d, Y, W, A, B, dX, G, stream=0)
+    dA, dB = torch.zeros(28, 64), torch.zeros(28, 32)
+    with pytest.raises(ValueError, match="device memory"):
+        P.plora_backward_dAdB(d, X, Y, H, G, dA, dB, None, stream=0)
+
+
+def test_desc_array_lengths(P):
+    """The descriptor's host arrays must have N + 1 offsets and N alphas: the
+    library reads them through raw pointers."""
+    with pytest.raises(ValueError, match="segment offsets"):
+        P.Desc([0, 3, 8], [4, 8, 16], [1.0, 1.0, 1.0], 64, 32)
+    with pytest.raises(ValueError, match="segment offsets"):
+        P.Desc([0, 3, 3, 8, 9], [4, 8, 16], [1.0, 1.0, 1.0], 64, 32)
+    with pytest.raises(ValueError, match="alphas"):
+        P.Desc([0, 3, 3, 8], [4, 8, 16], [1.0, 1.0], 64, 32)
+    with pytest.raises(ValueError, match="alphas"):
+        P.Desc([0, 3, 3, 8], [4, 8, 16], [1.0, 1.0, 1.0, 1.0], 64, 32)
+    assert P.plora_validate(P.Desc([0, 3, 3, 8], [4, 8, 16], [1.0, 1.0, 1.0], 64, 32)) == 0
+    assert P.plora_validate(P.Desc([], [], [], 64, 32, n_tokens=4)) == 0
+
+
 def test_profile_read_empty(P):
     P.plora_profile_reset()
     assert P.plora_profile_read("gemm_fwd") == (0, 0.0)
@@ -237,3 +271,11 @@ def test_dadb_acc_error_paths(P):
                                        None) == -8
     n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
     assert lib.plora_backward_dAdB_acc(n0.ref(), None, None, None, None, None, None, None, 0, 1, None) == 0
+
+
+def test_library_matches_sources(P):
+    """The loaded library was built from the sources in this tree (the package
+    refuses to load one that was not)."""
+    from packed_adapter_lora_amd.build import source_hash
+    assert P.plora_source_hash() == source_hash()
+    assert len(source_hash()) == 16
