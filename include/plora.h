@@ -193,6 +193,19 @@ int plora_adamw_step(const plora_desc* desc, const plora_adamw_config* cfg, floa
                      float* vA, float* mB, float* vB, const float* dA, const float* dB, void* A, void* B,
                      void* stream);
 
+/* The operator's copies of fp32 master panels: A = PA and B = PB in
+ * desc.dtype (bf16: each element rounded to nearest even; f32: a copy).
+ * Mixed-precision training keeps the adapters as fp32 masters and runs the
+ * operator on their bf16 copies [LoRA加速集成方案 (cloud.baidu.com), 三、核心组件
+ * > 2. 硬件加速 (mixed precision) and 七、使用建议]; plora_adamw_step writes the
+ * copies itself, this call is for masters changed by anything else.
+ *   PA  fp32 [R, d_in], PB fp32 [R, d_out] (read only)
+ *   A   desc.dtype [R, d_in], B desc.dtype [R, d_out] (overwritten; must not
+ *       overlap PA / PB)
+ * Only n_adapters, ranks, dtype, d_in and d_out of `desc` are used (it must
+ * still be valid).  All pointers 16-byte aligned.  N = 0 is a no-op. */
+int plora_cast_panels(const plora_desc* desc, const float* PA, const float* PB, void* A, void* B, void* stream);
+
 /* Number of fp32 elements of H (and of G): sum_i n_i r_i.  Returns 0 for an
  * invalid descriptor. */
 size_t plora_h_elems(const plora_desc* desc);

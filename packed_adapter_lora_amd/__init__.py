@@ -21,6 +21,7 @@ import numpy as np
 
 __all__ = [
     "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
+    "plora_adamw_step", "plora_cast_panels", "AdamwConfig",
     "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version", "plora_source_hash",
     "plora_profile_enable", "plora_profile_read", "plora_profile_reset", "LIB_PATH", "PLORA_F32", "PLORA_BF16",
 ]
@@ -90,6 +91,7 @@ def _load():
         "plora_backward_dAdB_acc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                                    vp]),
         "plora_adamw_step": (ctypes.c_int, [dp, ctypes.POINTER(plora_adamw_config)] + [vp] * 11),
+        "plora_cast_panels": (ctypes.c_int, [dp, vp, vp, vp, vp, vp]),
         "plora_rmsnorm_fwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                              vp]),
         "plora_rmsnorm_bwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64] + [vp] * 9),
@@ -291,6 +293,16 @@ def plora_adamw_step(desc: Desc, cfg: AdamwConfig, PA, PB, mA, vA, mB, vB, dA, d
                                  _addr(vB), _addr(dA), _addr(dB), _addr(A), _addr(B), _stream(stream)))
 
 
+def plora_cast_panels(desc: Desc, PA, PB, A, B, stream=None):
+    """The operator's desc.dtype copies A, B of the fp32 master panels PA, PB (see plora.h)."""
+    R, di, do = desc.R, int(desc.c.d_in), int(desc.c.d_out)
+    e = _elt(desc)
+    for n, t, shp, dt in (("PA", PA, (R, di), "float32"), ("PB", PB, (R, do), "float32"), ("A", A, (R, di), e),
+                          ("B", B, (R, do), e)):
+        _check_tensor(n, t, shp, dt)
+    _check(_lib.plora_cast_panels(desc.ref(), _addr(PA), _addr(PB), _addr(A), _addr(B), _stream(stream)))
+
+
 def plora_h_elems(desc: Desc) -> int:
     return int(_lib.plora_h_elems(desc.ref()))
 
@@ -451,3 +463,12 @@ def plora_plan_makespan(steps, mem_bytes, ms_per_step, mem_budget, fixed_ms, mem
     if v < 0:
         _check(int(v))
     return float(v)
+
+
+def __getattr__(name):
+    # the PyTorch module is imported on first use (the C-ABI binding itself
+    # needs only numpy and ctypes)
+    if name in ("PackedLoRALinear", "PackedLoRAFunction"):
+        from . import module
+        return getattr(module, name)
+    raise AttributeError(name)

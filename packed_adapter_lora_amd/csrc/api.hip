@@ -295,6 +295,28 @@ int plora_adamw_step(const plora_desc* d, const plora_adamw_config* cfg, float* 
     }
 }
 
+int plora_cast_panels(const plora_desc* d, const float* PA, const float* PB, void* A, void* B, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_adapters == 0) return PLORA_OK;
+        if (!PA || !PB || !A || !B) return fail(PLORA_ERR_NULL, "PA, PB, A and B are required");
+        if (misaligned(PA) || misaligned(PB) || misaligned(A) || misaligned(B))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        int64_t R = 0;
+        for (int i = 0; i < d->n_adapters; ++i) R += d->ranks[i];
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const int32_t bf = d->dtype == PLORA_BF16 ? 1 : 0;
+        hipError_t e = launch_cast_panel(PA, A, bf, R * d->d_in, st);
+        if (e != hipSuccess) return hip_fail(e, "cast launch");
+        e = launch_cast_panel(PB, B, bf, R * d->d_out, st);
+        if (e != hipSuccess) return hip_fail(e, "cast launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
 int plora_profile_enable(int on) {
     g_prof.on = on != 0;
     return PLORA_OK;

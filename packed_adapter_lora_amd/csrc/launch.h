@@ -78,6 +78,8 @@ struct AdamwArgs {
     int64_t D;
 };
 hipError_t launch_adamw(const AdamwArgs& a, const AdamwTable& t, hipStream_t st);
+// out[e] = dtype copy of P[e] for e < n (bf16: round to nearest even).
+hipError_t launch_cast_panel(const float* P, void* out, int32_t out_bf16, int64_t n, hipStream_t st);
 
 hipError_t launch_gemm_f32(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);
 hipError_t launch_shrink_f32(const ShrinkArgs& a, const SegTable& s, hipStream_t st);

@@ -60,7 +60,34 @@ __global__ __launch_bounds__(256) void adamw_panel(AdamwArgs a, AdamwTable t) {
     }
 }
 
+// out = dtype copy of the fp32 panel P (bf16: round to nearest even), 16-byte
+// accesses; one workgroup per 1024 elements.
+__global__ __launch_bounds__(256) void cast_panel(const float* __restrict__ P, void* __restrict__ out, int32_t out_bf16,
+                                                  int64_t n) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= n) return;  // n is a multiple of 8
+    const f32x4 p = *reinterpret_cast<const f32x4*>(P + e);
+    if (out_bf16) {
+        bf16x4 b;
+        b[0] = to_bf16(p[0]);
+        b[1] = to_bf16(p[1]);
+        b[2] = to_bf16(p[2]);
+        b[3] = to_bf16(p[3]);
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(out) + e) = b;
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = p;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_cast_panel(const float* P, void* out, int32_t out_bf16, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    const int64_t wg = (n + 1023) / 1024;
+    if (wg > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cast_panel, dim3((unsigned)wg), dim3(256), 0, st, P, out, out_bf16, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_adamw(const AdamwArgs& a, const AdamwTable& t, hipStream_t st) {
     const int R = t.roff[t.n];

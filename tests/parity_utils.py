@@ -6,6 +6,11 @@ one adapter's H, G, dA, dB) the error must satisfy both
 and, elementwise,
     |out - ref| <= tol * (|ref| + rms(ref_block))
 with tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulate).
+
+The fp32 outputs of bf16 problems (H, G, dA, dB) are held to 1e-4 as well:
+they are fp32 sums of exact bf16 products, and H/G enter the expand and the
+weight-gradient products as a bf16 hi/lo pair (about 2^-16 relative), so a
+loss of that precision (a single bf16 term, 2^-9) fails them.
 """
 from __future__ import annotations
 
@@ -14,6 +19,12 @@ import sys
 import numpy as np
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL_F32_OUT = 1e-4
+
+
+def tol_of(wl_dtype, name):
+    """Tolerance of output `name` for a problem of dtype wl_dtype."""
+    return TOL_F32_OUT if name in ("H", "G", "dA", "dB") else TOL[wl_dtype]
 
 
 def log(msg):
@@ -112,20 +123,21 @@ def h_blocks(wl):
 
 
 def check_full(wl, gpu, ref, tol=None, names=("Y", "H", "dX", "G", "dA", "dB")):
-    """Blockwise comparison of every output of a small problem."""
-    tol = TOL[wl.dtype] if tol is None else tol
+    """Blockwise comparison of every output of a small problem (tol: one
+    tolerance for every output instead of tol_of's)."""
+    t = (lambda k: tol_of(wl.dtype, k)) if tol is None else (lambda k: tol)
     if wl.n_adapters == 0:
         for k in ("Y", "dX"):
             if k in names and k in gpu:
-                check_block(gpu[k], ref[k], tol, k)
+                check_block(gpu[k], ref[k], t(k), k)
         return
     for i, rows, rr, hs, r, n in h_blocks(wl):
         for k in ("Y", "dX"):
             if k in names and k in gpu:
-                check_block(gpu[k][rows], ref[k][rows], tol, "%s[segment %d]" % (k, i))
+                check_block(gpu[k][rows], ref[k][rows], t(k), "%s[segment %d]" % (k, i))
         for k in ("H", "G"):
             if k in names and k in gpu:
-                check_block(gpu[k][hs], ref[k][hs], tol, "%s[adapter %d]" % (k, i))
+                check_block(gpu[k][hs], ref[k][hs], t(k), "%s[adapter %d]" % (k, i))
         for k in ("dA", "dB"):
             if k in names and k in gpu:
-                check_block(gpu[k][rr], ref[k][rr], tol, "%s[adapter %d]" % (k, i))
+                check_block(gpu[k][rr], ref[k][rr], t(k), "%s[adapter %d]" % (k, i))

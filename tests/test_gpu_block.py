@@ -270,3 +270,76 @@ def test_decoder_block_fwd_bwd(P):
     for n in PROJ:
         chain(grads[n][0], ref_grads[n][0], "dA[%s]" % n)
         chain(grads[n][1], ref_grads[n][1], "dB[%s]" % n)
+
+
+# ---------------------------------------------------------------------------
+# The decoder block at its full size: hidden 4096, 32 query / 8 key-value
+# heads, MLP 14336, 32 adapters (ranks cycling 8..64) of 1024 tokens each, one
+# sequence per adapter.  Attention stays inside a sequence and every other
+# kernel is row-wise, so a sequence's output and input-gradient rows and its
+# adapter's dA/dB on every projection depend on that sequence alone: the fp64
+# oracle runs on one sequence (as a one-adapter problem with that adapter's
+# A/B rows) and is compared with those rows and gradients of the full-size GPU
+# run.
+# ---------------------------------------------------------------------------
+
+FULL = dict(hidden=4096, n_q=32, n_kv=8, mlp=14336, n=32, L=1024, seed=71)
+
+
+def chained_check(got, ref, name):
+    """The chained-rounding bound of test_decoder_block_fwd_bwd: Frobenius
+    2e-2 and elementwise 2e-2 |ref| + 0.15 rms(ref)."""
+    got = host(got) if hasattr(got, "detach") else np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    check_block(got, ref, 2e-2, name, elementwise=False)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    lim = 2e-2 * np.abs(ref) + 0.15 * rms
+    log("%s: rel Frobenius %.2e, worst elementwise %.2f of the bound" % (
+        name, np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30), float(np.max(err / lim))))
+    assert np.all(err <= lim), "%s: %d elements beyond the chained-rounding bound" % (name, int(np.sum(err > lim)))
+
+
+@pytest.fixture(scope="module")
+def full_block(P):
+    import torch
+    from packed_adapter_lora_amd.block import DecoderBlock
+    f = FULL
+    ranks = [(8, 16, 32, 64)[i % 4] for i in range(f["n"])]
+    alphas = [(8.0, 16.0, 32.0)[i % 3] for i in range(f["n"])]
+    off = [i * f["L"] for i in range(f["n"] + 1)]
+    T = off[-1]
+    log("full-size decoder block T=%d hidden=%d heads=%d/%d mlp=%d adapters=%d" % (
+        T, f["hidden"], f["n_q"], f["n_kv"], f["mlp"], f["n"]))
+    hp, dp = block_params(f["hidden"], f["n_q"], f["n_kv"], f["mlp"], ranks, f["seed"])
+    x, dout = bf((T, f["hidden"]), f["seed"], 90), bf((T, f["hidden"]), f["seed"], 91)
+    blk = DecoderBlock(dp, off, ranks, alphas, off)
+    out = blk.forward(dev(x))
+    dx, grads = blk.backward(dev(dout))
+    torch.cuda.synchronize()
+    res = {"out": host(out), "dx": host(dx), "grads": {n: (host(a), host(b)) for n, (a, b) in grads.items()}}
+    del blk, out, dx, grads, dp
+    torch.cuda.empty_cache()
+    return hp, x, dout, ranks, alphas, off, res
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("seq", [0, 13, 31])
+def test_decoder_block_full_size(full_block, seq):
+    from packed_adapter_lora_amd.block import PROJ
+    hp, x, dout, ranks, alphas, off, res = full_block
+    a, b = off[seq], off[seq + 1]
+    r, ro = ranks[seq], sum(ranks[:seq])
+    L = b - a
+    log("sequence %d (rank %d, alpha %g): fp64 oracle on tokens %d..%d" % (seq, r, alphas[seq], a, b))
+    sub = dict(hp)
+    sub["A"] = {n: v[ro:ro + r] for n, v in hp["A"].items()}
+    sub["B"] = {n: v[ro:ro + r] for n, v in hp["B"].items()}
+    sub["ranks"], sub["alphas"] = np.array([r]), np.array([alphas[seq]])
+    ref_out, cache = OB.block_forward(sub, x[a:b], [0, L], [0, L], store=rnd)
+    ref_dx, ref_grads = OB.block_backward(sub, cache, dout[a:b], [0, L], [0, L], store=rnd)
+    chained_check(res["out"][a:b], ref_out, "out[sequence %d]" % seq)
+    chained_check(res["dx"][a:b], ref_dx, "dx[sequence %d]" % seq)
+    for n in PROJ:
+        chained_check(res["grads"][n][0][ro:ro + r], ref_grads[n][0], "dA[%s, adapter %d]" % (n, seq))
+        chained_check(res["grads"][n][1][ro:ro + r], ref_grads[n][1], "dB[%s, adapter %d]" % (n, seq))

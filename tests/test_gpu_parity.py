@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads
-from parity_utils import TOL, check_block, check_full, h_blocks, host, log, run_gpu, to_dev
+from parity_utils import TOL, check_block, check_full, h_blocks, host, log, run_gpu, to_dev, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -335,10 +335,8 @@ def sampled_case(P, wl, per_segment=4):
     for i, rws, rr, hs, r, n in h_blocks(wl):
         one = oracle.packed_lora([0, n], [r], [float(wl.alphas[i])], wl.d_in, wl.d_out, X=inp["X"][rws],
                                  dY=inp["dY"][rws], A=inp["A"][rr], B=inp["B"][rr], want=("H", "G", "dA", "dB"))
-        check_block(Hg[hs], one["H"], tol, "H[adapter %d]" % i)
-        check_block(Gg[hs], one["G"], tol, "G[adapter %d]" % i)
-        check_block(dA[rr], one["dA"], tol, "dA[adapter %d]" % i)
-        check_block(dB[rr], one["dB"], tol, "dB[adapter %d]" % i)
+        for k, g in (("H", Hg[hs]), ("G", Gg[hs]), ("dA", dA[rr]), ("dB", dB[rr])):
+            check_block(g, one[k], tol_of(wl.dtype, k), "%s[adapter %d]" % (k, i))
     del gpu
     torch.cuda.empty_cache()
 

@@ -212,6 +212,51 @@ def test_rank1_closed_form(with_w):
 
 
 # --------------------------------------------------------------------------
+# rank-r closed form on the inputs of the GPU indexing probe
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("set_name", ["le64", "r128"])
+def test_rank_r_probe_closed_form(set_name):
+    """With A_i's columns distinct unit vectors e_k (k in K_i), B_i = c_i * ones,
+    0/1 rows X, one-hot dY (column n_t) and a -1/0/+1 weight, for t in S_i:
+      H[t, j] = X[t, k_ij]             G[t, j] = c_i
+      Y[t]    = X[t] W^T + s_i c_i sum_j X[t, k_ij]
+      dX[t]   = W[n_t] + s_i c_i on the columns K_i
+      dA_i[j] = s_i c_i sum_t X[t]     dB_i[j, n] = s_i * #{t : X[t, k_ij] = 1, n_t = n}
+    all exact small integers times powers of two (the GPU probe compares
+    against the oracle bit for bit on the same inputs)."""
+    from exact_probe import ADAPTER_SETS, probe_inputs
+    cfg = ADAPTER_SETS[set_name]
+    counts, ranks, svals = cfg["counts"], cfg["ranks"], np.array(cfg["scales"])
+    d_in, d_out = 512, 96
+    inp, ks, nt, c = probe_inputs(counts, ranks, d_in, d_out, seed=3)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    alphas = svals * np.asarray(ranks)
+    out = oracle.packed_lora(off, ranks, alphas, d_in, d_out, **inp)
+    X, W = inp["X"].astype(np.float64), inp["W"].astype(np.float64)
+    T, R = X.shape[0], sum(ranks)
+    Y, dX = np.zeros((T, d_out)), np.zeros((T, d_in))
+    H, G = np.zeros(out["H"].shape), np.zeros(out["G"].shape)
+    dA, dB = np.zeros((R, d_in)), np.zeros((R, d_out))
+    ro, ho = 0, 0
+    for i, r in enumerate(ranks):
+        cols = ks[ro:ro + r]
+        for t in range(int(off[i]), int(off[i + 1])):
+            m = X[t, cols]
+            Y[t] = X[t] @ W.T + svals[i] * c[i] * m.sum()
+            dX[t] = W[nt[t]]
+            dX[t, cols] += svals[i] * c[i]
+            H[ho:ho + r] = m
+            G[ho:ho + r] = c[i]
+            ho += r
+            dA[ro:ro + r] += svals[i] * c[i] * X[t]
+            dB[ro + np.arange(r), nt[t]] += svals[i] * m
+        ro += r
+    for k, v in (("Y", Y), ("dX", dX), ("H", H), ("G", G), ("dA", dA), ("dB", dB)):
+        assert np.array_equal(out[k], v), k
+
+
+# --------------------------------------------------------------------------
 # backward = gradient of the forward (central differences, L affine per entry)
 # --------------------------------------------------------------------------
 
