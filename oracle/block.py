@@ -235,9 +235,12 @@ def block_forward(p, x, seg, seq, store=identity, eps=RMS_EPS, store_f32=store32
     return out, c
 
 
-def block_backward(p, c, dout, seg, seq, store=identity):
+def block_backward(p, c, dout, seg, seq, store=identity, keep=None):
     """Backward of the block from the forward's cache; returns (dx, grads)
-    with grads[name] = (dA, dB) for every projection (fp64)."""
+    with grads[name] = (dA, dB) for every projection (fp64).  keep: an
+    optional dict that receives the gradient entering the attention
+    ("datt") and the attention's outputs before the rotary adjoint ("dq",
+    "dk", "dv")."""
     dout = np.asarray(dout, np.float64)
     grads = {}
 
@@ -254,6 +257,8 @@ def block_backward(p, c, dout, seg, seq, store=identity):
     dx2 = store(dout + rmsnorm_bwd(dh2, c["x2"], p["w2"], c["r2"]))
     datt = bwd("o", c["att"], dx2, c["Ho"])
     dq, dk, dv = attention_bwd(datt, c["qr"], c["kr"], c["v"], c["att"], c["lse"], seq, p["n_q"], p["n_kv"])
+    if keep is not None:
+        keep.update(datt=datt, dq=dq, dk=dk, dv=dv)
     pos = positions_of(seq)
     dq, dk, dv = store(rope_bwd(store(dq), pos)), store(rope_bwd(store(dk), pos)), store(dv)
     dh1 = bwd("q", c["h1"], dq, c["Hq"]) + bwd("k", c["h1"], dk, c["Hk"]) + bwd("v", c["h1"], dv, c["Hv"])

@@ -91,9 +91,12 @@ class DecoderBlock:
         self.cache = c
         return out
 
-    def backward(self, dout, stream=None):
+    def backward(self, dout, stream=None, keep=False):
         """dout: bf16 [T, hidden].  Returns (dx, grads) with grads[name] =
-        (dA, dB) fp32 for every projection."""
+        (dA, dB) fp32 for every projection.  keep: also hold the gradient
+        entering the attention ("datt"), the attention's input gradients after
+        the rotary adjoint ("dq", "dk", "dv") and the residual-stream gradient
+        below the MLP ("dx2") in self.cache["bwd"]."""
         p, T, c = self.p, self.T, self.cache
         grads = {}
         R = int(self.desc["q"].R)
@@ -123,4 +126,6 @@ class DecoderBlock:
         dh1 = [bwd("q", c["h1"], dq, c["Hq"]), bwd("k", c["h1"], dk, c["Hk"]), bwd("v", c["h1"], dv, c["Hv"])]
         dx = self._bf(T, self.hidden)
         plora_rmsnorm_bwd(dh1, c["x"], p["w1"], c["r1"], dx, dres=dx2, stream=stream)
+        if keep:
+            c["bwd"] = {"datt": datt, "dq": dq, "dk": dk, "dv": dv, "dx2": dx2}
         return dx, grads

@@ -213,6 +213,47 @@ def bwd_rounding_bounds(q, k, v, dO, o, lse, offs, n_q, n_kv):
     return bq, bk, bv
 
 
+@pytest.mark.slow
+def test_attention_full_size_32_sequences(P):
+    """Attention forward and backward at the decoder block's full size: 32
+    sequences of 1024 tokens, 32 query / 8 key-value heads (the work order of
+    many sequences), checked per kernel, as above, on three sampled sequences
+    (each sequence's attention depends on its own rows only)."""
+    import torch
+    n_q, n_kv, L, n = 32, 8, 1024, 32
+    offs = [i * L for i in range(n + 1)]
+    T = offs[-1]
+    log("attention fwd+bwd %d sequences x %d tokens, heads %d/%d" % (n, L, n_q, n_kv))
+    q, k, v = attn_inputs(offs, n_q, n_kv, 68)
+    dO = bf((T, n_q * 128), 68, 4)
+    o = torch.full((T, n_q * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((n_q, T), float("nan"), dtype=torch.float32, device="cuda")
+    P.plora_attention_fwd(dev(q), dev(k), dev(v), o, lse, offs, n_q, n_kv)
+    outs = [torch.full((T, nh * 128), float("nan"), dtype=torch.bfloat16, device="cuda") for nh in (n_q, n_kv, n_kv)]
+    delta = torch.full((n_q, T), float("nan"), dtype=torch.float32, device="cuda")
+    # the backward from the GPU's own forward outputs (o, lse)
+    P.plora_attention_bwd(dev(q), dev(k), dev(v), o, lse, dev(dO), *outs, delta, offs, n_q, n_kv)
+    torch.cuda.synchronize()
+    o_h, lse_h = host(o), host(lse)
+    outs_h = [host(t) for t in outs]
+    for sq in (0, 13, 31):
+        a, b = offs[sq], offs[sq + 1]
+        log("sequence %d" % sq)
+        one = [0, L]
+        o_ref, lse_ref = OB.attention_fwd(q[a:b], k[a:b], v[a:b], one, n_q, n_kv)
+        check_attention_out(o_h[a:b], o_ref, one, n_q, "o[seq %d]" % sq)
+        np.testing.assert_allclose(lse_h[:, a:b], lse_ref, rtol=1e-5, atol=1e-4)
+        refs = OB.attention_bwd(dO[a:b], q[a:b], k[a:b], v[a:b], o_h[a:b], lse_h[:, a:b], one, n_q, n_kv)
+        bounds = bwd_rounding_bounds(q[a:b], k[a:b], v[a:b], dO[a:b], o_h[a:b], lse_h[:, a:b], one, n_q, n_kv)
+        for name, got, ref, nh, bd in zip(("dq", "dk", "dv"), outs_h, refs, (n_q, n_kv, n_kv), bounds):
+            got = got[a:b]
+            check_attention_out(got, ref, one, nh, "%s[seq %d]" % (name, sq), elementwise=False)
+            err = np.abs(got - ref)
+            lim = 2.0 * (bd + 2.0 ** -9 * np.abs(ref)) + 1e-6
+            assert np.all(err <= lim), "%s[seq %d]: %d elements beyond the rounding bound; worst ratio %.2f" % (
+                name, sq, int(np.sum(err > lim)), float(np.max(err / lim)))
+
+
 def block_params(hidden, n_q, n_kv, mlp, ranks, seed):
     import torch
     from packed_adapter_lora_amd.block import proj_dims
@@ -286,7 +327,7 @@ def test_decoder_block_fwd_bwd(P):
 FULL = dict(hidden=4096, n_q=32, n_kv=8, mlp=14336, n=32, L=1024, seed=71)
 
 
-def chained_check(got, ref, name):
+def chained_check(got, ref, name, elementwise=True):
     """The chained-rounding bound of test_decoder_block_fwd_bwd: Frobenius
     2e-2 and elementwise 2e-2 |ref| + 0.15 rms(ref)."""
     got = host(got) if hasattr(got, "detach") else np.asarray(got, np.float64)
@@ -295,6 +336,10 @@ def chained_check(got, ref, name):
     rms = float(np.sqrt(np.mean(ref * ref)))
     err = np.abs(got - ref)
     lim = 2e-2 * np.abs(ref) + 0.15 * rms
+    if not elementwise:
+        log("%s: rel Frobenius %.2e (elementwise: link by link below)" % (
+            name, np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)))
+        return
     log("%s: rel Frobenius %.2e, worst elementwise %.2f of the bound" % (
         name, np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30), float(np.max(err / lim))))
     assert np.all(err <= lim), "%s: %d elements beyond the chained-rounding bound" % (name, int(np.sum(err > lim)))
@@ -315,16 +360,49 @@ def full_block(P):
     x, dout = bf((T, f["hidden"]), f["seed"], 90), bf((T, f["hidden"]), f["seed"], 91)
     blk = DecoderBlock(dp, off, ranks, alphas, off)
     out = blk.forward(dev(x))
-    dx, grads = blk.backward(dev(dout))
+    dx, grads = blk.backward(dev(dout), keep=True)
     torch.cuda.synchronize()
     res = {"out": host(out), "dx": host(dx), "grads": {n: (host(a), host(b)) for n, (a, b) in grads.items()}}
-    del blk, out, dx, grads, dp
+    c, cb = blk.cache, blk.cache["bwd"]
+    rows = np.concatenate([np.arange(off[i], off[i + 1]) for i in FULL_SEQS])
+    rt = torch.from_numpy(rows).cuda()
+    # the GPU's own intermediates on the sampled sequences' rows: q and k after
+    # the rotary embedding, v, the attention output and statistics, and the
+    # backward's attention gradients, dq and dk after the rotary adjoint
+    res["mid"] = {k: (rows, host(t[rt])) for k, t in (("q", c["q"]), ("k", c["k"]), ("v", c["v"]),
+                                                       ("att", c["att"]), ("datt", cb["datt"]), ("dq", cb["dq"]),
+                                                       ("dk", cb["dk"]), ("dv", cb["dv"]), ("dx2", cb["dx2"]))}
+    res["mid"]["lse"] = (rows, host(c["lse"][:, rt]))
+    res["mid"]["r1"] = (rows, host(c["r1"][rt]))
+    del blk, out, dx, grads, dp, c, cb
     torch.cuda.empty_cache()
     return hp, x, dout, ranks, alphas, off, res
 
 
+FULL_SEQS = (0, 13, 31)
+
+
+def rope_abs(e, positions):
+    """Elementwise bound after the rotary adjoint: each element of a rotated
+    pair is at most |cos| e_same + |sin| e_other."""
+    T = e.shape[0]
+    eh = e.reshape(T, -1, 128)
+    ang = OB.rope_angles(positions)[:, None, :]
+    c, s = np.abs(np.cos(ang)), np.abs(np.sin(ang))
+    lo, hi = eh[..., :64], eh[..., 64:]
+    return np.concatenate([lo * c + hi * s, hi * c + lo * s], axis=-1).reshape(T, -1)
+
+
+def gpu_rows(res, key, a, b):
+    """The GPU's intermediate `key` on token rows a..b-1 (kept by the fixture)."""
+    rows, vals = res["mid"][key]
+    i = int(np.searchsorted(rows, a))
+    assert rows[i] == a and rows[i + b - a - 1] == b - 1
+    return vals[..., i:i + b - a] if key == "lse" else vals[i:i + b - a]
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("seq", [0, 13, 31])
+@pytest.mark.parametrize("seq", FULL_SEQS)
 def test_decoder_block_full_size(full_block, seq):
     from packed_adapter_lora_amd.block import PROJ
     hp, x, dout, ranks, alphas, off, res = full_block
@@ -339,7 +417,44 @@ def test_decoder_block_full_size(full_block, seq):
     ref_out, cache = OB.block_forward(sub, x[a:b], [0, L], [0, L], store=rnd)
     ref_dx, ref_grads = OB.block_backward(sub, cache, dout[a:b], [0, L], [0, L], store=rnd)
     chained_check(res["out"][a:b], ref_out, "out[sequence %d]" % seq)
-    chained_check(res["dx"][a:b], ref_dx, "dx[sequence %d]" % seq)
+    # dx lies below both attention kernels, which feed P and dS to the matrix
+    # cores in bf16 while the oracle's attention is fp64 by definition; in the
+    # block the scores are large (the adapters' branches dominate q and k), so
+    # that rounding is amplified.  End to end dx is held to the Frobenius
+    # bound; elementwise it is checked link by link from the GPU's own
+    # intermediates: attention forward and backward at their per-kernel
+    # rounding bounds, then the rest of the chain (rotary adjoint, the q/k/v
+    # input gradients, the first RMSNorm's backward) at the chained bound.
+    chained_check(res["dx"][a:b], ref_dx, "dx[sequence %d]" % seq, elementwise=False)
+    one, n_q, n_kv = [0, L], sub["n_q"], sub["n_kv"]
+    q, k, v = (gpu_rows(res, key, a, b) for key in ("q", "k", "v"))
+    att, lse, datt = gpu_rows(res, "att", a, b), gpu_rows(res, "lse", a, b), gpu_rows(res, "datt", a, b)
+    o_ref, lse_ref = OB.attention_fwd(q, k, v, one, n_q, n_kv)
+    check_attention_out(att, o_ref, one, n_q, "attention o[sequence %d]" % seq)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-5, atol=1e-4)
+    pos = OB.positions_of(one)
+    refs = OB.attention_bwd(datt, q, k, v, att, lse, one, n_q, n_kv)
+    bounds = bwd_rounding_bounds(q, k, v, datt, att, lse, one, n_q, n_kv)
+    for name, ref, bd, nh in zip(("dq", "dk", "dv"), refs, bounds, (n_q, n_kv, n_kv)):
+        got = gpu_rows(res, name, a, b)
+        lim = 2.0 * (bd + 2.0 ** -9 * np.abs(ref)) + 1e-6
+        if name != "dv":
+            # the GPU's dq, dk are kept after the rotary adjoint: an orthogonal
+            # map of each pair, whose kernel rounds its output to bf16 again
+            ref = OB.rope_bwd(ref, pos)
+            lim = rope_abs(lim, pos) + 2.0 * 2.0 ** -9 * np.abs(ref)
+        check_attention_out(got, ref, one, nh, "attention %s[sequence %d]" % (name, seq), elementwise=False)
+        err = np.abs(got - ref)
+        log("attention %s[sequence %d]: worst elementwise %.2f of the rounding bound" % (
+            name, seq, float(np.max(err / lim))))
+        assert np.all(err <= lim), "attention %s[sequence %d]: %d elements beyond the rounding bound" % (
+            name, seq, int(np.sum(err > lim)))
+    dh1 = 0.0
+    for name in ("q", "k", "v"):
+        dh1 = dh1 + rnd(OB._proj(sub, name, one, ("dX",), dY=gpu_rows(res, "d" + name, a, b))["dX"])
+    r1 = gpu_rows(res, "r1", a, b)
+    tail = rnd(gpu_rows(res, "dx2", a, b) + OB.rmsnorm_bwd(dh1, x[a:b], sub["w1"], r1))
+    chained_check(res["dx"][a:b], tail, "dx[sequence %d] from the GPU's attention gradients" % seq)
     for n in PROJ:
         chained_check(res["grads"][n][0][ro:ro + r], ref_grads[n][0], "dA[%s, adapter %d]" % (n, seq))
         chained_check(res["grads"][n][1][ro:ro + r], ref_grads[n][1], "dB[%s, adapter %d]" % (n, seq))
