@@ -152,6 +152,23 @@ int plora_backward_dAdB_acc(const plora_desc* desc, const void* X, const void* d
                             const float* G, float* dA, float* dB, void* workspace,
                             size_t workspace_bytes, int accumulate, void* stream);
 
+/* plora_backward_dAdB_acc without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * or training loops, harnesses that forbid hipMalloc.  Nothing is allocated
+ * per call: the workspace lives in a library-owned device array of
+ * PLORA_NOALLOC_SCRATCH_BYTES (256 MiB), one per device, held from the
+ * library's first use of that device until the process ends.  A descriptor
+ * whose plora_workspace_bytes() exceeds that size returns PLORA_ERR_WORKSPACE
+ * before anything is enqueued.  The array is not cleared between calls (the
+ * kernels write whatever they read from it).  All calls on one device share
+ * the array: calls that overlap on one GPU (other streams, or threads
+ * without ordering between their calls) race.  Otherwise the arguments,
+ * results and errors are those of plora_backward_dAdB_acc; the device is the
+ * current one. */
+#define PLORA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int plora_backward_dAdB_noalloc(const plora_desc* desc, const void* X, const void* dY, const float* H,
+                                const float* G, float* dA, float* dB, int accumulate, void* stream);
+
 /* Per-adapter AdamW over the packed adapter panels.
  *
  * The fine-tuning loop that trains the LoRA parameters uses AdamW with

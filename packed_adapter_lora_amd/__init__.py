@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
-    "plora_adamw_step", "plora_cast_panels", "AdamwConfig",
+    "plora_adamw_step", "plora_cast_panels", "AdamwConfig", "plora_backward_dAdB_noalloc",
     "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version", "plora_source_hash",
     "plora_profile_enable", "plora_profile_read", "plora_profile_reset", "LIB_PATH", "PLORA_F32", "PLORA_BF16",
 ]
@@ -90,6 +90,7 @@ def _load():
         "plora_backward_dAdB": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]),
         "plora_backward_dAdB_acc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                                    vp]),
+        "plora_backward_dAdB_noalloc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, ctypes.c_int, vp]),
         "plora_adamw_step": (ctypes.c_int, [dp, ctypes.POINTER(plora_adamw_config)] + [vp] * 11),
         "plora_cast_panels": (ctypes.c_int, [dp, vp, vp, vp, vp, vp]),
         "plora_rmsnorm_fwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp, vp,
@@ -252,6 +253,18 @@ def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=
         nbytes = plora_workspace_bytes(desc)
     _check(_lib.plora_backward_dAdB_acc(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA), _addr(dB),
                                         _addr(workspace), nbytes, 1 if accumulate else 0, _stream(stream)))
+
+
+def plora_backward_dAdB_noalloc(desc: Desc, X, dY, H, G, dA, dB, accumulate=False, stream=None):
+    """plora_backward_dAdB without a workspace (the library's per-device scratch array; see plora.h)."""
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    he = plora_h_elems(desc)
+    for n, t, s, d in (("X", X, (T, di), e), ("dY", dY, (T, do), e), ("H", H, (he,), "float32"),
+                       ("G", G, (he,), "float32"), ("dA", dA, (R, di), "float32"), ("dB", dB, (R, do), "float32")):
+        _check_tensor(n, t, s, d)
+    _check(_lib.plora_backward_dAdB_noalloc(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA),
+                                            _addr(dB), 1 if accumulate else 0, _stream(stream)))
 
 
 class AdamwConfig:

@@ -279,3 +279,19 @@ def test_library_matches_sources(P):
     from packed_adapter_lora_amd.build import source_hash
     assert P.plora_source_hash() == source_hash()
     assert len(source_hash()) == 16
+
+
+def test_noalloc_error_paths(P):
+    """The no-allocation entry point validates on the host before it looks up
+    its scratch: invalid descriptors and problems whose workspace exceeds the
+    scratch array return their codes without touching a GPU."""
+    lib = P._lib
+    bad = desc(P, ranks=(4, 0, 16))
+    assert lib.plora_backward_dAdB_noalloc(bad.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0, None) == -3
+    # 200000 tokens of one rank-128 adapter over d_in = 4096: 196 chunks of partials (411 MB)
+    huge = desc(P, counts=(200000,), ranks=(128,), alphas=(1.0,), d_in=4096, d_out=16384)
+    assert P.plora_workspace_bytes(huge) > (256 << 20)
+    rc = lib.plora_backward_dAdB_noalloc(huge.ref(), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0, None)
+    assert rc == -8 and "scratch" in P.plora_last_error()
+    n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
+    assert lib.plora_backward_dAdB_noalloc(n0.ref(), None, None, None, None, None, None, 1, None) == 0
