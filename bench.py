@@ -209,37 +209,86 @@ def workload_label(wl):
     return "%s_%dx%d_%d_adapters_%s" % (family, wl.d_in, wl.d_out, wl.n_adapters, mix)
 
 
-def run_bench(wl, steps, warmup):
+class Stepper:
+    """Buffers and one training step (forward, backward_dx, backward_dAdB) of
+    the operator on device inputs `dev` for descriptor `d` (n_adapters = 0
+    runs the frozen path only)."""
+
+    def __init__(self, P, d, dev, T, d_in, d_out, R):
+        import torch
+        self.P, self.d, self.dev = P, d, dev
+        he = P.plora_h_elems(d) if R else 0
+        dt = dev["X"].dtype
+        self.Y = torch.empty((T, d_out), dtype=dt, device="cuda")
+        self.dX = torch.empty((T, d_in), dtype=dt, device="cuda")
+        self.H = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he] if R else None
+        self.G = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he] if R else None
+        self.dA = torch.empty((max(R, 1), d_in), dtype=torch.float32, device="cuda")[:R]
+        self.dB = torch.empty((max(R, 1), d_out), dtype=torch.float32, device="cuda")[:R]
+        nb = P.plora_workspace_bytes(d) if R else 0
+        self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
+        self.R = R
+        self.stream = torch.cuda.current_stream()
+
+    def step(self):
+        P, d, dev, st = self.P, self.d, self.dev, self.stream
+        A, B = (dev["A"], dev["B"]) if self.R else (None, None)
+        P.plora_forward(d, dev["X"], dev["W"], A, B, self.Y, self.H, st)
+        P.plora_backward_dx(d, dev["dY"], dev["W"], A, B, self.dX, self.G, st)
+        if self.R:
+            P.plora_backward_dAdB(d, dev["X"], dev["dY"], self.H, self.G, self.dA, self.dB, self.ws, st)
+
+
+def timed_steps(stepper, steps, warmup, flush=None):
+    """Wall-clock seconds per step over `steps` steps (synchronised on both
+    sides), plus each step's duration from a HIP event pair on the launch
+    stream.  flush: a tensor rewritten before every step (evicts L2 and the
+    Infinity Cache; the rewrite lies outside the events, and the wall clock
+    then includes it, so only the event figures are used)."""
+    import torch
+    for _ in range(warmup):
+        stepper.step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        if flush is not None:
+            flush.fill_(float(k))
+        ev[k][0].record()
+        stepper.step()
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return (t1 - t0) / steps, per
+
+
+def summary_ms(per):
+    n = len(per)
+    return {"median": round(per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2]), 4),
+            "mean": round(sum(per) / n, 4), "min": round(per[0], 4), "max": round(per[-1], 4)}
+
+
+def run_bench(wl, steps, warmup, dev=None):
+    """The timed region: `steps` steps after `warmup` with the library's
+    per-kernel HIP events on (the roofline's kernel durations).  Returns
+    (seconds per step, per-kernel figures, host inputs, stepper)."""
     import torch
     import packed_adapter_lora_amd as P
-    inp, dev = make_device_inputs(wl)
+    inp = None
+    if dev is None:
+        inp, dev = make_device_inputs(wl)
     d = P.Desc.from_workload(wl)
-    he = P.plora_h_elems(d)
-    dt = dev["X"].dtype
-    Y = torch.empty((wl.T, wl.d_out), dtype=dt, device="cuda")
-    dX = torch.empty((wl.T, wl.d_in), dtype=dt, device="cuda")
-    H = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he]
-    G = torch.empty((max(he, 4),), dtype=torch.float32, device="cuda")[:he]
-    dA = torch.empty((wl.R, wl.d_in), dtype=torch.float32, device="cuda")
-    dB = torch.empty((wl.R, wl.d_out), dtype=torch.float32, device="cuda")
-    nb = P.plora_workspace_bytes(d)
-    ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step():
-        P.plora_forward(d, dev["X"], dev["W"], dev["A"], dev["B"], Y, H, stream)
-        P.plora_backward_dx(d, dev["dY"], dev["W"], dev["A"], dev["B"], dX, G, stream)
-        P.plora_backward_dAdB(d, dev["X"], dev["dY"], H, G, dA, dB, ws, stream)
-
+    stp = Stepper(P, d, dev, wl.T, wl.d_in, wl.d_out, wl.R)
     for _ in range(warmup):
-        step()
+        stp.step()
     torch.cuda.synchronize()
     P.plora_profile_reset()
     P.plora_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        stp.step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     P.plora_profile_enable(False)
@@ -248,11 +297,131 @@ def run_bench(wl, steps, warmup):
         n, ms = P.plora_profile_read(cls)
         kern[cls] = {"launches": n, "mean_ms": (ms / n) if n else 0.0, "ms_per_step": ms / steps}
     P.plora_profile_reset()
-    if wl.n_adapters:
-        kern["adamw"] = run_adamw(P, wl, d, dev, dA, dB, steps, warmup)
-    del Y, dX, H, G, dA, dB, ws, dev
+    return (t1 - t0) / steps, kern, inp, stp
+
+
+def measure_ceilings():
+    """Measured ceilings (include/plora_probe.h): sustained bf16 matrix-core
+    throughput on random register operands, HBM copy and read bandwidth.
+    Median of 5 timed launches after one warm-up."""
+    import torch
+    import packed_adapter_lora_amd as P
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    nb = P.plora_probe_mfma_operand_bytes()
+    ops = torch.randn((nb // 2,), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    wg = 2 * cus
+    out = torch.empty((wg * 256,), dtype=torch.float32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    iters = 40000
+    fl = [0.0]
+
+    def mf():
+        fl[0] = P.plora_probe_mfma(ops, wg, iters, out)
+
+    ms = timed(mf)
+    res = {"mfma_bf16_tflops": round(fl[0] / (ms * 1e-3) / 1e12, 1),
+           "mfma_probe": "%d workgroups x 4 waves, %d x 16 v_mfma_f32_32x32x16_bf16 each on random bf16 register "
+                         "operands; %.2f ms" % (wg, iters, ms)}
+    zeros = torch.zeros_like(ops)
+
+    def mz():
+        P.plora_probe_mfma(zeros, wg, iters, out)
+
+    res["mfma_bf16_tflops_zero_operands"] = round(fl[0] / (timed(mz, 3) * 1e-3) / 1e12, 1)
+    del zeros, ops
+    nbytes = 2 << 30
+    src = torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: P.plora_probe_copy(src, dst, 8 * cus))
+    res["hbm_copy_GBps"] = round(2.0 * nbytes / (ms * 1e-3) / 1e9, 1)
+    red = torch.empty((8 * cus * 256,), dtype=torch.int32, device="cuda")
+    ms = timed(lambda: P.plora_probe_read(src, red, 8 * cus))
+    res["hbm_read_GBps"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    res["hbm_probe"] = "2 GiB, %d workgroups of 256 threads, 16-byte accesses" % (8 * cus)
+    del src, dst, red, out
     torch.cuda.empty_cache()
-    return (t1 - t0) / steps, kern, inp
+    return res
+
+
+def smi_sample():
+    """One reading of the GPU's power and clocks from amd-smi (JSON), reduced
+    to the fields whose names mention power or a clock; None if unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], stdout=subprocess.PIPE,
+                           stderr=subprocess.DEVNULL, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    flat = {}
+
+    def walk(x, pre):
+        if isinstance(x, dict):
+            if "value" in x and not isinstance(x["value"], (dict, list)):
+                flat[pre] = x["value"]
+                return
+            for k, v in x.items():
+                walk(v, pre + "." + str(k) if pre else str(k))
+        elif isinstance(x, list):
+            if x and not isinstance(x[0], (dict, list)):
+                return
+            for k, v in enumerate(x[:1]):
+                walk(v, pre)
+        else:
+            flat[pre] = x
+    walk(data, "")
+    keep = {k: v for k, v in flat.items() if ("power" in k.lower() or "clk" in k.lower() or "clock" in k.lower())
+            and isinstance(v, (int, float)) and ("gfx" in k.lower() or "power" in k.lower() or "mem" in k.lower())}
+    return dict(list(keep.items())[:24]) or None
+
+
+def clock_record(stepper, seconds=3.0):
+    """Power and clock readings (amd-smi) taken while the step runs back to
+    back for about `seconds`, next to idle readings from before."""
+    import threading
+    import torch
+    idle = smi_sample()
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = smi_sample()
+            if v:
+                samples.append(v)
+            stop.wait(0.3)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            stepper.step()
+        torch.cuda.synchronize()
+        n += 10
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return {"available": False, "note": "amd-smi gave no reading"}
+    keys = sorted(set().union(*samples))
+    load = {k: round(float(np.median([s[k] for s in samples if k in s])), 1) for k in keys}
+    return {"available": True, "idle": idle, "under_load_median": load, "samples": len(samples),
+            "steps_run": n, "source": "amd-smi metric --power --clock --json"}
 
 
 def run_adamw(P, wl, d, dev, dA, dB, steps, warmup):
@@ -285,13 +454,14 @@ def run_adamw(P, wl, d, dev, dA, dB, steps, warmup):
             "achieved_GBps": nbytes / (per_call * 1e-3) / 1e9 if per_call else 0.0}
 
 
-def run_loop_bench(wl, steps, warmup):
+def run_loop_bench(wl, steps, warmup, dev=None):
     """The same tokens computed adapter by adapter: one single-adapter call per
     segment for each of forward, backward_dx and backward_dAdB (the sequential
     execution that packing replaces).  Returns seconds per step."""
     import torch
     import packed_adapter_lora_amd as P
-    _, dev = make_device_inputs(wl)
+    if dev is None:
+        _, dev = make_device_inputs(wl)
     dt = dev["X"].dtype
     Y = torch.empty((wl.T, wl.d_out), dtype=dt, device="cuda")
     dX = torch.empty((wl.T, wl.d_in), dtype=dt, device="cuda")
@@ -328,7 +498,6 @@ def run_loop_bench(wl, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     del Y, dX, H, G, dA, dB, dev
-    torch.cuda.empty_cache()
     return (t1 - t0) / steps
 
 
@@ -350,9 +519,40 @@ def cpu_baseline(wl, inp, per_segment):
     oracle.packed_lora(sub_off, wl.ranks, wl.alphas.astype(np.float64), wl.d_in, wl.d_out, X=X, dY=dY, W=W, A=A,
                        B=B, want=("Y", "H", "dX", "G", "dA", "dB"))
     dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    threads = oracle.threads()
+    # one core: the first 4 tokens of every segment
+    rows1 = np.concatenate([np.arange(int(wl.offsets[i]), min(int(wl.offsets[i + 1]), int(wl.offsets[i]) + 4))
+                            for i in range(wl.n_adapters)])
+    seg1 = np.searchsorted(wl.offsets, rows1, side="right") - 1
+    off1 = np.concatenate([[0], np.cumsum(np.bincount(seg1, minlength=wl.n_adapters))]).astype(np.int64)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.packed_lora(off1, wl.ranks, wl.alphas.astype(np.float64), wl.d_in, wl.d_out,
+                           X=inp["X"][rows1].astype(np.float64), dY=inp["dY"][rows1].astype(np.float64), W=W, A=A,
+                           B=B, want=("Y", "H", "dX", "G", "dA", "dB"))
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "first %d tokens of each of the %d segments (%d tokens), full d_in x d_out, all of Y, H, dX, "
-                      "G, dA, dB over them; %.1f s" % (per_segment, wl.n_adapters, len(rows), dt)}
+                      "G, dA, dB over them; %.1f s on %d threads" % (per_segment, wl.n_adapters, len(rows), dt,
+                                                                     threads),
+            "nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model,
+            "single_core": {"value": len(rows1) / dt1, "unit": "tokens/s", "threads": 1,
+                            "sample": "first 4 tokens of each segment (%d tokens); %.1f s" % (len(rows1), dt1)}}
 
 
 BLOCK_DIMS = {"hidden": 4096, "n_q": 32, "n_kv": 8, "mlp": 14336}
@@ -668,6 +868,9 @@ def main():
     ap.add_argument("--adapters", type=int, default=None)
     ap.add_argument("--cpu-tokens", type=int, default=64, help="oracle sample: tokens per segment")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
+    ap.add_argument("--no-clock", action="store_true", help="skip the power and clock record")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the adapter sweep of the default run")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--plan", action="store_true",
                     help="plan a 120-job LoRA search with the packing planner (cost model fitted on the GPU)")
@@ -735,8 +938,10 @@ def main():
 
     wl = workloads.config(args.workload, n_adapters=args.adapters)
     log("workload %s: T=%d d_in=%d d_out=%d N=%d R=%d" % (wl.name, wl.T, wl.d_in, wl.d_out, wl.n_adapters, wl.R))
-    sec, kern, inp = run_bench(wl, args.steps, args.warmup)
-    opt = kern.pop("adamw", None)
+    import packed_adapter_lora_amd as P
+    log("step 1: timed region (%d steps after %d warm-up, per-kernel events on)" % (args.steps, args.warmup))
+    sec, kern, inp, stp = run_bench(wl, args.steps, args.warmup)
+    dev = stp.dev
     tokens_per_s = wl.T / sec
     dom = max(("gemm_fwd", "gemm_bwd"), key=lambda k: kern[k]["mean_ms"])
     flops = gemm_flops(wl, dom)
@@ -746,9 +951,48 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, wl), "kernel": dom,
             "flops_per_launch": flops, "mean_launch_ms": round(kern[dom]["mean_ms"], 4)}
     whole = step_flops(wl) / sec / 1e12
+    log("step 2: the same step without per-kernel events (per-step event timings)")
+    _, per = timed_steps(stp, args.steps, 2)
+    step_ms = {"timed_region_mean": round(sec * 1e3, 4), "unprofiled": summary_ms(per)}
+    log("step 3: with L2 and the Infinity Cache flushed before every step")
+    import torch
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    _, perf = timed_steps(stp, args.steps, 2, flush=flush)
+    del flush
+    step_ms["cache_flushed"] = summary_ms(perf)
+    log("step 4: frozen path only (no adapters) on the same tokens")
+    d0 = P.Desc([0], [], [], wl.d_in, wl.d_out, wl.dtype, n_tokens=wl.T)
+    s0 = Stepper(P, d0, {k: dev[k] for k in ("X", "W", "dY")}, wl.T, wl.d_in, wl.d_out, 0)
+    _, per0 = timed_steps(s0, args.steps, 2)
+    del s0
+    frozen = summary_ms(per0)
+    overhead = {"frozen_ms_per_step": frozen["median"],
+                "lora_overhead_ms": round(step_ms["unprofiled"]["median"] - frozen["median"], 4),
+                "lora_overhead_frac": round((step_ms["unprofiled"]["median"] - frozen["median"]) /
+                                            step_ms["unprofiled"]["median"], 4)}
+    opt = None
+    if wl.n_adapters:
+        log("step 5: per-adapter AdamW on the step's gradients")
+        opt = run_adamw(P, wl, stp.d, dev, stp.dA, stp.dB, args.steps, args.warmup)
+    ceil = None
+    if not args.no_ceilings:
+        log("step 6: measured ceilings (sustained MFMA, HBM copy/read)")
+        ceil = measure_ceilings()
+        roof["peak_measured"] = ceil["mfma_bf16_tflops"]
+        roof["frac_of_measured"] = round(achieved / ceil["mfma_bf16_tflops"], 4)
+    clock = None
+    if not args.no_clock:
+        log("step 7: power and clock while the step runs")
+        clock = clock_record(stp)
+    sweep = None
+    if not args.no_sweep and wl.name == "llama_up" and wl.n_adapters == 32:
+        log("step 8: adapter sweep (2..32 adapters x 2048 tokens, 4096->14336 and 4096->4096)")
+        sweep = adapter_sweep(wl, dev, max(5, args.steps // 2))
+    del stp
+    torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu:
-        log("timing the oracle on the host ...")
+        log("step 9: timing the oracle on the host ...")
         cpu = cpu_baseline(wl, inp, args.cpu_tokens)
     out = {
         "metric": "packed LoRA fwd+bwd tokens/sec at %d adapters" % wl.n_adapters,
@@ -768,8 +1012,13 @@ def main():
             "ranks": sorted(set(wl.ranks.tolist())), "sum_ranks": wl.R},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "step_ms": step_ms,
+        "lora_overhead": overhead,
         "whole_step_tflops": round(whole, 1),
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kern.items()},
+        "ceilings": ceil,
+        "clock": clock,
+        "adapter_sweep": sweep,
     }
     if opt:
         # the per-adapter AdamW step over the packed panels, timed after (not in) the step above
@@ -782,15 +1031,65 @@ def main():
     if args.sweep:
         for n in (2, 4, 8, 16, 32):
             w2 = workloads.config(args.workload, n_adapters=n)
-            s2, k2, _ = run_bench(w2, args.steps, args.warmup)
-            k2.pop("adamw", None)
+            s2, k2, _, st2 = run_bench(w2, args.steps, args.warmup)
+            del st2
             s3 = run_loop_bench(w2, max(3, args.steps // 4), 2)
+            torch.cuda.empty_cache()
             print(json.dumps({"sweep": True, "workload": w2.name, "n_adapters": n, "tokens": w2.T,
                               "tokens_per_s": round(w2.T / s2, 1), "ms_per_step": round(s2 * 1e3, 4),
                               "adapter_by_adapter_tokens_per_s": round(w2.T / s3, 1),
                               "packing_gain": round(s3 / s2, 3),
                               "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in k2.items()}}),
                   flush=True)
+
+
+def slice_inputs(dev, wl_n):
+    """Device inputs of the first N adapters of a workload whose per-adapter
+    draws and 2048-row chunks do not depend on N: the first T_N token rows and
+    the first R_N rank rows are exactly the N-adapter workload's inputs."""
+    return {"W": dev["W"], "A": dev["A"][:wl_n.R], "B": dev["B"][:wl_n.R], "X": dev["X"][:wl_n.T],
+            "dY": dev["dY"][:wl_n.T]}
+
+
+def adapter_sweep(wl, dev, steps):
+    """Tokens/s of the packed step at N = 2..32 adapters of 2048 tokens on the
+    4096->14336 and 4096->4096 shapes, against the same tokens computed
+    adapter by adapter (median of per-step events; the loop by wall clock)."""
+    import torch
+    import packed_adapter_lora_amd as P
+    import workloads
+    res = {}
+    shapes = [("llama_up", dev)]
+    sq = workloads.config("llama_sq", n_adapters=32)
+    inp_sq = workloads.make_inputs(sq, which=("W", "B", "dY"))
+    dt = dev["X"].dtype
+    dev_sq = {"W": torch.from_numpy(inp_sq["W"]).to("cuda").to(dt), "A": dev["A"],  # A and X: the same draws
+              "B": torch.from_numpy(inp_sq["B"]).to("cuda").to(dt), "X": dev["X"],
+              "dY": torch.from_numpy(inp_sq["dY"]).to("cuda").to(dt)}
+    del inp_sq
+    shapes.append(("llama_sq", dev_sq))
+    for name, dv in shapes:
+        rows = []
+        for n in (2, 4, 8, 16, 32):
+            w2 = workloads.config(name, n_adapters=n)
+            sub = slice_inputs(dv, w2)
+            stp = Stepper(P, P.Desc.from_workload(w2), sub, w2.T, w2.d_in, w2.d_out, w2.R)
+            _, per = timed_steps(stp, steps, 2)
+            del stp
+            med = summary_ms(per)["median"]
+            loop = run_loop_bench(w2, max(3, steps // 2), 1, dev=sub)
+            rows.append({"n_adapters": n, "tokens": w2.T, "ms_per_step": med,
+                         "tokens_per_s": round(w2.T / (med * 1e-3), 1),
+                         "adapter_by_adapter_tokens_per_s": round(w2.T / loop, 1),
+                         "packing_gain": round(loop / (med * 1e-3), 3)})
+        ref = rows[-1]["tokens_per_s"]
+        for r in rows:
+            r["vs_32"] = round(r["tokens_per_s"] / ref, 3)
+        res[name] = rows
+        torch.cuda.empty_cache()
+    del dev_sq
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

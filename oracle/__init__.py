@@ -61,6 +61,8 @@ def _load():
             lib.oracle_h_elems.argtypes = [ctypes.c_int, i64p, i32p]
             lib.oracle_threads.restype = ctypes.c_int
             lib.oracle_threads.argtypes = []
+            lib.oracle_set_threads.restype = None
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -79,7 +81,7 @@ class use_library:
         _load()
         self._saved = _lib
         lib = ctypes.CDLL(self.path)
-        for name in ("oracle_packed_lora", "oracle_check", "oracle_h_elems", "oracle_threads"):
+        for name in ("oracle_packed_lora", "oracle_check", "oracle_h_elems", "oracle_threads", "oracle_set_threads"):
             f, g = getattr(lib, name), getattr(self._saved, name)
             f.restype, f.argtypes = g.restype, g.argtypes
         _lib = lib
@@ -93,6 +95,11 @@ class use_library:
 
 def threads() -> int:
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of later oracle calls (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _f64(a):

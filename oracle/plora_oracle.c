@@ -80,6 +80,16 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Number of threads later calls may use (n >= 1); results do not depend on it
+ * (threads split independent rows and output columns only). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Mathematical preconditions of the problem: a partition of the T tokens
  * into N contiguous, possibly empty, segments (o_0 = 0, o_N = T); ranks in
  * 1..128; finite alphas.  With N = 0 there is no adapter and every token takes

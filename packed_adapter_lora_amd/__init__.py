@@ -109,6 +109,11 @@ def _load():
         "plora_plan_makespan": (ctypes.c_double, [ctypes.POINTER(plora_job), ctypes.c_int32,
                                                   ctypes.POINTER(plora_pack_model), ctypes.POINTER(ctypes.c_int32),
                                                   ctypes.c_int32]),
+        "plora_probe_mfma_operand_bytes": (ctypes.c_size_t, []),
+        "plora_probe_mfma": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_double),
+                                            vp]),
+        "plora_probe_copy": (ctypes.c_int, [vp, vp, ctypes.c_size_t, ctypes.c_int32, vp]),
+        "plora_probe_read": (ctypes.c_int, [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
         "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
         "plora_validate": (ctypes.c_int, [dp]),
@@ -314,6 +319,47 @@ def plora_cast_panels(desc: Desc, PA, PB, A, B, stream=None):
                           ("B", B, (R, do), e)):
         _check_tensor(n, t, shp, dt)
     _check(_lib.plora_cast_panels(desc.ref(), _addr(PA), _addr(PB), _addr(A), _addr(B), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Ceiling micro-benchmarks (include/plora_probe.h): device buffers as torch
+# tensors; each call enqueues one kernel on the stream.
+# ---------------------------------------------------------------------------
+
+def plora_probe_mfma_operand_bytes() -> int:
+    return int(_lib.plora_probe_mfma_operand_bytes())
+
+
+def plora_probe_mfma(operands, workgroups, iters, out, stream=None) -> float:
+    """Enqueues the sustained-MFMA probe; returns the launch's FLOP count."""
+    if operands.numel() * operands.element_size() < plora_probe_mfma_operand_bytes():
+        raise ValueError("operand buffer smaller than plora_probe_mfma_operand_bytes()")
+    if out.numel() < workgroups * 256 or str(out.dtype) != "torch.float32":
+        raise ValueError("out needs workgroups * 256 fp32 values")
+    for n, t in (("operands", operands), ("out", out)):
+        _check_tensor(n, t, tuple(t.shape), None)
+    fl = ctypes.c_double(0.0)
+    _check(_lib.plora_probe_mfma(_addr(operands), int(workgroups), int(iters), _addr(out), ctypes.byref(fl),
+                                 _stream(stream)))
+    return float(fl.value)
+
+
+def plora_probe_copy(src, dst, workgroups=2048, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    for n, t in (("src", src), ("dst", dst)):
+        _check_tensor(n, t, tuple(t.shape), None)
+    _check(_lib.plora_probe_copy(_addr(src), _addr(dst), nbytes, int(workgroups), _stream(stream)))
+
+
+def plora_probe_read(src, out, workgroups=2048, stream=None):
+    if out.numel() < workgroups * 256 or out.element_size() != 4:
+        raise ValueError("out needs workgroups * 256 32-bit values")
+    for n, t in (("src", src), ("out", out)):
+        _check_tensor(n, t, tuple(t.shape), None)
+    _check(_lib.plora_probe_read(_addr(src), src.numel() * src.element_size(), int(workgroups), _addr(out),
+                                 _stream(stream)))
 
 
 def plora_h_elems(desc: Desc) -> int:

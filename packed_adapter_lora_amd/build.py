@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libplora.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["api.hip", "api_noalloc.hip", "api_block.hip", "gemm_bf16.hip", "lora_bf16.hip", "kernels_f32.hip", "optim.hip",
-               "block.hip", "attention.hip", "attention_dkv.hip"]
+               "block.hip", "attention.hip", "attention_dkv.hip", "probes.hip"]
 CXX_SOURCES = ["plan.cpp", "planner.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
