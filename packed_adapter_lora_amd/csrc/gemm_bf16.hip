@@ -920,11 +920,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
         for (int n = 0; n < 4; ++n)
             fb[s][n] = as_bf16x8(*reinterpret_cast<const u32x4*>(bt + kmaj(wq * 128 + n * 32 + l32, 2 * kk + lh)));
     };
+    // serpentine order: consecutive instructions share one operand (the chip is
+    // power-capped and its clock follows how much the operands toggle); every
+    // accumulator still sees its k-steps in order, so the bits do not change
     auto mm = [&](int s) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) acc[m][n] = mfma32x32x16(fa[s][m], fb[s][n], acc[m][n]);
+            for (int n0 = 0; n0 < 4; ++n0) {
+                const int n = (m & 1) ? 3 - n0 : n0;
+                acc[m][n] = mfma32x32x16(fa[s][m], fb[s][n], acc[m][n]);
+            }
     };
     // 4*NM MFMAs interleaved with NM + 4 fragment reads (and `dma` LDS DMA loads)
     auto sched = [&](int dma) {
