@@ -311,8 +311,7 @@ def measure_ceilings():
     g.manual_seed(1234)
     nb = P.plora_probe_mfma_operand_bytes()
     ops = torch.randn((nb // 2,), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    wg = 2 * cus
-    out = torch.empty((wg * 256,), dtype=torch.float32, device="cuda")
+    out = torch.empty((cus * 256,), dtype=torch.float32, device="cuda")
 
     def timed(fn, reps=5):
         fn()
@@ -327,22 +326,35 @@ def measure_ceilings():
             ts.append(a.elapsed_time(b))
         return sorted(ts)[len(ts) // 2]
 
-    iters = 40000
-    fl = [0.0]
+    def sustained(shape, o, seconds=1.5):
+        """TFLOP/s of back-to-back launches (a few ms each) over the last half
+        of `seconds`, after the power controller has settled."""
+        iters, fl = 12000, [0.0]
+        fn = lambda: fl.__setitem__(0, P.plora_probe_mfma(o, wg, iters, out, shape=shape))
+        t0, n, e0 = time.perf_counter(), 0, None
+        while time.perf_counter() - t0 < seconds:
+            if e0 is None and time.perf_counter() - t0 > seconds / 2:
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            for _ in range(4):
+                fn()
+                n += 1 if e0 is not None else 0
+            torch.cuda.synchronize()
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        torch.cuda.synchronize()
+        return fl[0] * n / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
-    def mf():
-        fl[0] = P.plora_probe_mfma(ops, wg, iters, out)
-
-    ms = timed(mf)
-    res = {"mfma_bf16_tflops": round(fl[0] / (ms * 1e-3) / 1e12, 1),
-           "mfma_probe": "%d workgroups x 4 waves, %d x 16 v_mfma_f32_32x32x16_bf16 each on random bf16 register "
-                         "operands; %.2f ms" % (wg, iters, ms)}
+    wg = cus  # one wave per SIMD
+    t32 = sustained(0, ops)
+    t16 = sustained(1, ops)
     zeros = torch.zeros_like(ops)
-
-    def mz():
-        P.plora_probe_mfma(zeros, wg, iters, out)
-
-    res["mfma_bf16_tflops_zero_operands"] = round(fl[0] / (timed(mz, 3) * 1e-3) / 1e12, 1)
+    z32 = sustained(0, zeros)
+    res = {"mfma_bf16_tflops": round(max(t32, t16), 1), "mfma_32x32x16_tflops": round(t32, 1),
+           "mfma_16x16x32_tflops": round(t16, 1), "mfma_32x32x16_zero_operands_tflops": round(z32, 1),
+           "mfma_probe": "%d workgroups x 4 waves (one per SIMD), each a 128x128 block of accumulators in registers "
+                         "fed random bf16 operands, back-to-back launches for 1.5 s, the last 0.75 s timed" % wg}
     del zeros, ops
     nbytes = 2 << 30
     src = torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda")

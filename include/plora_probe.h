@@ -11,8 +11,8 @@
  * these probes reach on the same GPU:
  *
  *   plora_probe_mfma   sustained bf16 matrix-core throughput: every wave
- *                      issues v_mfma_f32_32x32x16_bf16 back to back on random
- *                      operands held in registers (fresh fragments every
+ *                      issues matrix-core instructions back to back on random
+ *                      operands held in registers (operands changing every
  *                      instruction, no memory traffic in the loop)
  *   plora_probe_copy   HBM bandwidth of a plain device copy (16-byte accesses)
  *   plora_probe_read   HBM bandwidth of a plain read
@@ -39,12 +39,17 @@ size_t plora_probe_mfma_operand_bytes(void);
 
 /* One launch of `workgroups` workgroups of 4 waves; each wave loads its 16
  * fragments from `operands` (slice (4 * workgroup + wave) mod 1024) and runs
- * `iters` iterations of 16 matrix-core instructions.
+ * `iters` iterations of 128 x 128 x 32 multiply-adds on a 128 x 128 block of
+ * fp32 accumulators held in registers:
+ *   shape 0  32 v_mfma_f32_32x32x16_bf16 per iteration (4 x 4 accumulators, in
+ *            serpentine order: consecutive instructions share one operand),
+ *   shape 1  64 v_mfma_f32_16x16x32_bf16 per iteration (8 x 8, row by row).
+ * One workgroup per compute unit puts one wave on every SIMD.
  *   out    device fp32, workgroups * 256 values (each lane's accumulator sum)
  *   flops  host: receives the launch's floating-point operation count
- *          (workgroups * 4 * iters * 16 * 2 * 32 * 32 * 16) */
-int plora_probe_mfma(const void* operands, int32_t workgroups, int32_t iters, float* out, double* flops,
-                     void* stream);
+ *          (workgroups * 4 * iters * 2 * 128 * 128 * 32) */
+int plora_probe_mfma(const void* operands, int32_t shape, int32_t workgroups, int32_t iters, float* out,
+                     double* flops, void* stream);
 
 /* dst[0..bytes) = src[0..bytes) with `workgroups` workgroups of 256 threads,
  * grid-stride; bytes a multiple of 16; the buffers must not overlap.  Moves

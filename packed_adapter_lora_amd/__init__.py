@@ -110,8 +110,8 @@ def _load():
                                                   ctypes.POINTER(plora_pack_model), ctypes.POINTER(ctypes.c_int32),
                                                   ctypes.c_int32]),
         "plora_probe_mfma_operand_bytes": (ctypes.c_size_t, []),
-        "plora_probe_mfma": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_double),
-                                            vp]),
+        "plora_probe_mfma": (ctypes.c_int, [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp,
+                                            ctypes.POINTER(ctypes.c_double), vp]),
         "plora_probe_copy": (ctypes.c_int, [vp, vp, ctypes.c_size_t, ctypes.c_int32, vp]),
         "plora_probe_read": (ctypes.c_int, [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
@@ -330,8 +330,9 @@ def plora_probe_mfma_operand_bytes() -> int:
     return int(_lib.plora_probe_mfma_operand_bytes())
 
 
-def plora_probe_mfma(operands, workgroups, iters, out, stream=None) -> float:
-    """Enqueues the sustained-MFMA probe; returns the launch's FLOP count."""
+def plora_probe_mfma(operands, workgroups, iters, out, shape=0, stream=None) -> float:
+    """Enqueues the sustained-MFMA probe (shape 0: 32x32x16, 1: 16x16x32);
+    returns the launch's FLOP count."""
     if operands.numel() * operands.element_size() < plora_probe_mfma_operand_bytes():
         raise ValueError("operand buffer smaller than plora_probe_mfma_operand_bytes()")
     if out.numel() < workgroups * 256 or str(out.dtype) != "torch.float32":
@@ -339,8 +340,8 @@ def plora_probe_mfma(operands, workgroups, iters, out, stream=None) -> float:
     for n, t in (("operands", operands), ("out", out)):
         _check_tensor(n, t, tuple(t.shape), None)
     fl = ctypes.c_double(0.0)
-    _check(_lib.plora_probe_mfma(_addr(operands), int(workgroups), int(iters), _addr(out), ctypes.byref(fl),
-                                 _stream(stream)))
+    _check(_lib.plora_probe_mfma(_addr(operands), int(shape), int(workgroups), int(iters), _addr(out),
+                                 ctypes.byref(fl), _stream(stream)))
     return float(fl.value)
 
 

@@ -2,14 +2,14 @@
 // kernels are held against: sustained bf16 matrix-core throughput with random
 // register operands, and HBM bandwidth of a plain copy and a plain read.
 //
-// mfma_probe: every wave keeps 8 A and 8 B fragments of random bf16 values in
-// registers (from the caller's operand buffer, a different slice per wave)
-// and issues v_mfma_f32_32x32x16_bf16 back to back over four independent
-// accumulators, each instruction on a different pair of fragments, so the
-// multipliers see fresh data every instruction as in a GEMM's inner loop (the
-// chip's clock under load depends on how much the operands toggle).  No
-// memory traffic inside the loop.  Each lane writes the sum of its
-// accumulators at the end, so nothing is optimised away.
+// mfma probes: every wave keeps 8 A and 8 B fragments of random bf16 values
+// in registers (from the caller's operand buffer, a different slice per wave)
+// and issues matrix-core instructions back to back over a 128 x 128 block of
+// accumulators, the operands changing from instruction to instruction as in a
+// GEMM's inner loop (the chip is power-capped, and its clock under load
+// depends on how much the operands toggle).  No memory traffic inside the
+// loop.  Each lane writes the sum of its accumulators at the end, so nothing
+// is optimised away.
 //
 // copy_probe / read_probe: 16-byte accesses, grid-stride over the buffer.
 #include <string>
@@ -24,31 +24,75 @@ namespace {
 
 constexpr int kProbeSlots = 1024;  // wave slices of the operand buffer (16 fragments x 64 lanes x 16 B each)
 
-__global__ __launch_bounds__(256) void mfma_probe(const u32x4* __restrict__ ops, int32_t iters, float* __restrict__ out) {
-    const int l = lane_id();
+// shape 0: v_mfma_f32_32x32x16_bf16 on a 4 x 4 block of accumulators (a
+// 128 x 128 wave tile) in serpentine order (consecutive instructions share one
+// operand), as in the GEMM's K loop, two sets of fragments alternating; shape
+// 1: v_mfma_f32_16x16x32_bf16 on 8 x 8 (the same tile), row by row (in
+// serpentine order the compiler shuffles these accumulators between
+// registers at every instruction).
+__device__ __forceinline__ void probe_frags(const u32x4* ops, bf16x8 (&a)[8], bf16x8 (&b)[8]) {
     const int slot = (int)(((int64_t)blockIdx.x * 4 + wave_id()) % kProbeSlots);
-    const u32x4* p = ops + (int64_t)slot * 16 * 64 + l;
-    bf16x8 a[8], b[8];
+    const u32x4* p = ops + (int64_t)slot * 16 * 64 + lane_id();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         a[k] = as_bf16x8(p[k * 64]);
         b[k] = as_bf16x8(p[(8 + k) * 64]);
     }
-    f32x16 acc[4];
+}
+
+__global__ __launch_bounds__(256) void mfma_probe32(const u32x4* __restrict__ ops, int32_t iters,
+                                                    float* __restrict__ out) {
+    bf16x8 a[8], b[8];
+    probe_frags(ops, a, b);
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x16{};
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc[k & 3] = mfma32x32x16(a[k], b[k], acc[k & 3]);
-            acc[(k + 2) & 3] = mfma32x32x16(a[k], b[(k + 3) & 7], acc[(k + 2) & 3]);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j0 = 0; j0 < 4; ++j0) {
+                    const int j = (i & 1) ? 3 - j0 : j0;
+                    acc[i][j] = mfma32x32x16(a[4 * h + i], b[4 * h + j], acc[i][j]);
+                }
     }
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s += acc[j][v];
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma_probe16(const u32x4* __restrict__ ops, int32_t iters,
+                                                    float* __restrict__ out) {
+    bf16x8 a[8], b[8];
+    probe_frags(ops, a, b);
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s += acc[i][j][v];
     out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
@@ -72,14 +116,21 @@ extern "C" {
 
 size_t plora_probe_mfma_operand_bytes(void) { return (size_t)kProbeSlots * 16 * 64 * 16; }
 
-int plora_probe_mfma(const void* operands, int32_t workgroups, int32_t iters, float* out, double* flops,
+int plora_probe_mfma(const void* operands, int32_t shape, int32_t workgroups, int32_t iters, float* out, double* flops,
                      void* stream) {
     if (!operands || !out || !flops) return fail(PLORA_ERR_NULL, "operands, out and flops are required");
     if (workgroups <= 0 || iters <= 0) return fail(PLORA_ERR_SHAPE, "workgroups and iters must be positive");
+    if (shape != 0 && shape != 1) return fail(PLORA_ERR_SHAPE, "shape must be 0 (32x32x16) or 1 (16x16x32)");
     if (misaligned(operands) || misaligned(out)) return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
-    *flops = (double)workgroups * 4.0 * (double)iters * 16.0 * (2.0 * 32 * 32 * 16);
-    hipLaunchKernelGGL(mfma_probe, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const u32x4*>(operands), iters, out);
+    // both shapes: 128 x 128 x 32 multiply-adds per wave and iteration
+    *flops = (double)workgroups * 4.0 * (double)iters * (2.0 * 128 * 128 * 32);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (shape == 0)
+        hipLaunchKernelGGL(mfma_probe32, dim3((unsigned)workgroups), dim3(256), 0, st,
+                           static_cast<const u32x4*>(operands), iters, out);
+    else
+        hipLaunchKernelGGL(mfma_probe16, dim3((unsigned)workgroups), dim3(256), 0, st,
+                           static_cast<const u32x4*>(operands), iters, out);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? PLORA_OK : hip_fail(e, "mfma probe launch");
 }
