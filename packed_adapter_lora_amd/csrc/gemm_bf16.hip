@@ -839,11 +839,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     constexpr int WL = 2 * NM;           // weight-tile loads per wave and stage
     using PR = PRows<NM>;
     const int64_t T = a.T, K = a.K, Pdim = a.Pdim;
+    const int64_t pb = a.p_begin, pe = a.p_end > 0 ? a.p_end : Pdim;
     const int tiles_q = (int)((T + kBQ - 1) / kBQ);
-    const int tiles_p = (int)((Pdim + BP - 1) / BP);
+    const int tiles_p = (int)((pe - pb + BP - 1) / BP);
     int tq, tp;
     tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, tq, tp);
-    const int64_t q0 = (int64_t)tq * kBQ, p0 = (int64_t)tp * BP;
+    const int64_t q0 = (int64_t)tq * kBQ, p0 = pb + (int64_t)tp * BP;
     const int l = lane_id(), w = wave_id();
     const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
 
@@ -1028,25 +1029,53 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
                            a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
                            (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
     if (pipelined) {
-        // 128-wide tiles when all of them fit on the chip at once (a few hundred
-        // tokens): each takes ~0.57 of a 256-wide tile's time.  With more tiles
-        // than CUs the 256-wide ones win, partial last waves included (fewer
-        // busy CUs run at a higher clock).  PLORA_GEMM_TILE_P=128 or 256 forces
-        // the width (same results either way: each output element sees the same
-        // MFMA sequence).
-        const int64_t cus = cu_count(), nwg2 = tq * ((a.Pdim + 127) / 128);
+        // Tile widths.  A 128-wide tile takes ~0.57 of a 256-wide tile's time.
+        // All 128-wide when they fit on the chip at once (a few hundred tokens).
+        // Otherwise the feature range is split: 256-wide tiles over the first
+        // f columns of 256 features, 128-wide over the rest, as two launches,
+        // with f chosen by counting waves (one unit per wave of 256-wide tiles,
+        // 0.57 per wave of 128-wide): a grid of 3.5 waves of 256-wide tiles
+        // becomes 3 waves plus one wave of 128-wide tiles.  Each output element
+        // sees the same MFMA sequence at either width, so the split does not
+        // change any bit.  PLORA_GEMM_TILE_P=128 or 256 forces one width.
+        const int64_t cus = cu_count(), tp2 = (a.Pdim + 127) / 128, nwg2 = tq * tp2;
         const char* force = getenv("PLORA_GEMM_TILE_P");
         const int fw = force ? atoi(force) : 0;
-        const bool half = fw == 128 || (fw != 256 && nwg2 <= cus);
-        const dim3 grid((unsigned)(half ? nwg2 : nwg));
-        if (p_kmajor && half)
-            hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 2>), grid, block, 0, st, a, s);
-        else if (p_kmajor)
-            hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 4>), grid, block, 0, st, a, s);
-        else if (half)
-            hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 2>), grid, block, 0, st, a, s);
-        else
-            hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4>), grid, block, 0, st, a, s);
+        int64_t f = tp;  // 256-wide feature columns
+        if (fw == 128 || (fw != 256 && nwg2 <= cus)) {
+            f = 0;
+        } else if (fw != 256) {
+            auto waves = [&](int64_t n) { return (n + cus - 1) / cus; };
+            double best = (double)waves(nwg);
+            for (int64_t g = tp - 1; g >= 0; --g) {
+                const int64_t rest = (a.Pdim - 256 * g + 127) / 128;
+                const double c = (double)waves(tq * g) + 0.57 * (double)waves(tq * rest);
+                if (c < best - 1e-9) {
+                    best = c;
+                    f = g;
+                }
+            }
+        }
+        if (f > 0) {
+            GemmArgs w = a;
+            w.p_begin = 0;
+            w.p_end = f == tp ? 0 : 256 * f;
+            const dim3 grid((unsigned)(tq * f));
+            if (p_kmajor)
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 4>), grid, block, 0, st, w, s);
+            else
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4>), grid, block, 0, st, w, s);
+        }
+        if (f < tp) {
+            GemmArgs h = a;
+            h.p_begin = 256 * f;
+            h.p_end = 0;
+            const dim3 grid((unsigned)(tq * ((a.Pdim - 256 * f + 127) / 128)));
+            if (p_kmajor)
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 2>), grid, block, 0, st, h, s);
+            else
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 2>), grid, block, 0, st, h, s);
+        }
     } else {
         const dim3 grid((unsigned)nwg);
         if (p_kmajor)

@@ -21,6 +21,9 @@ struct GemmArgs {
     void* O;          // Y or dX, [T][Pdim]
     int64_t T, K, Pdim;
     int32_t lora;     // 0: frozen path only
+    // feature range [p_begin, p_end) covered by one launch of the pipelined
+    // kernel (p_end = 0: up to Pdim); Pdim stays the row length and bound
+    int64_t p_begin, p_end;
 };
 
 // Shrink: out[hoff_i + (t - o_i) r_i + j] = sum_k Q[t][k] P[R_off[i]+j][k]

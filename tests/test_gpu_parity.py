@@ -374,3 +374,25 @@ def test_decode_shapes_full(P, name):
     per token tile), compared in full (forward only is what serving runs; the
     backward is covered too)."""
     full_case(P, workloads.config(name))
+
+
+@pytest.mark.slow
+def test_mixed_tile_widths_bitwise_equal(P, monkeypatch):
+    """qwen_q-sized GEMMs (64 x 14 = 896 tiles of 256 x 256, 3.5 waves on 256
+    compute units) run as 256-wide tiles over part of the features and
+    128-wide tiles over the rest, in two launches: the result equals a single
+    width bit for bit (each output element sees the same MFMA sequence)."""
+    import torch
+    wl = workloads.config("qwen_q")
+    log("case %s T=%d (mixed tile widths)" % (wl.name, wl.T))
+    dev = device_inputs(wl, workloads.make_inputs(wl))
+    out = {}
+    for mode in ("", "256", "128"):
+        if mode:
+            monkeypatch.setenv("PLORA_GEMM_TILE_P", mode)
+        else:
+            monkeypatch.delenv("PLORA_GEMM_TILE_P", raising=False)
+        out[mode] = run_gpu(P, wl, dev, want=("fwd", "dx"))
+    for mode in ("256", "128"):
+        for k in ("Y", "dX"):
+            assert torch.equal(out[""][k].view(torch.int16), out[mode][k].view(torch.int16)), (mode, k)
