@@ -125,7 +125,7 @@ int plora_forward(const plora_desc* d, const void* X, const void* W, const void*
         const bool bf = d->dtype == PLORA_BF16;
         hipError_t e = hipSuccess;
         if (lora) {
-            const ShrinkArgs sa{X, A, H, d->d_in, Y, d->d_out * 2};
+            const ShrinkArgs sa{X, A, H, d->d_in, Y, d->d_out * 2, 0};
             if (bf) {
                 WorkMap m;
                 const int32_t units = build_shrink_map(s, &m);
@@ -162,7 +162,7 @@ int plora_backward_dx(const plora_desc* d, const void* dY, const void* W, const 
         const bool bf = d->dtype == PLORA_BF16;
         hipError_t e = hipSuccess;
         if (lora) {
-            const ShrinkArgs sa{dY, B, G, d->d_out, dX, d->d_in * 2};
+            const ShrinkArgs sa{dY, B, G, d->d_out, dX, d->d_in * 2, 0};
             if (bf) {
                 WorkMap m;
                 const int32_t units = build_shrink_map(s, &m);

@@ -35,6 +35,7 @@ struct ShrinkArgs {
     int64_t K;
     void* scratch;       // output activation (Y or dX), free until the GEMM writes it
     int64_t scratch_row; // its bytes per token row (0: no K slices)
+    int32_t split_all;   // K slices for every adapter whose partials fit (not only single-tile ones)
 };
 
 // Weight gradient: out[R_off[i]+j][c] = s_i sum_{t in S_i} F_i[t-o_i][j] Q[t][c]

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
     const int64_t K = a.K;
     const int i = adapter_of_unit(m, seg.n, unit);
     const int64_t s0 = seg.off[i], s1 = seg.off[i + 1];
-    const int nsl = shrink_slices(s1 - s0, seg.rank[i], K, a.scratch_row);
+    const int nsl = shrink_slices(s1 - s0, seg.rank[i], K, a.scratch_row, a.split_all != 0);
     const int u = unit - m.pre[i], slice = u % nsl;
     const int64_t t0 = s0 + (int64_t)(u / nsl) * TR;
     const int nrows = (int)(s1 - t0 < TR ? s1 - t0 : TR);
@@ -154,8 +154,9 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
     // DMA block b: rows 8b .. 8b+7; lane l -> row 8b + l/8, physical chunk l%8
     const int r0 = l >> 3;
     const uint32_t lane_row = (uint32_t)(r0 * K * 2);
-    // this work item's stages: [kt0, kt1) of the K / 64
+    // this work item's stages: [kt0, kt1) of the K / 64 (one K quarter per slice)
     const int KT = (int)(K / 64), kt0 = slice * KT / nsl, kt1 = (slice + 1) * KT / nsl;
+    const int nq = shrink_quarters(K);
     // token tile: blocks 4w .. 4w+3 (32 rows per wave); panel: 4*MAXJT blocks,
     // PB per wave
     constexpr int PB = 4 * MAXJT / WPG;
@@ -175,9 +176,22 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + kShX + blk * 1024), 16, vo, 0, 0, 0);
         }
     };
-    f32x16 acc[MAXJT];
+    f32x16 acc[MAXJT], tot[MAXJT];
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = f32x16{};
+    for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = tot[jt] = f32x16{};
+    int q = nsl == 1 ? 0 : slice;  // the K quarter being accumulated
+    // after stage kt: at the end of quarter q, total = q0 (or this slice's
+    // quarter) or total + q, and the accumulator restarts from zero
+    auto fold = [&](int kt) {
+        if (kt + 1 != (q + 1) * KT / nq) return;
+#pragma unroll
+        for (int jt = 0; jt < MAXJT; ++jt) {
+            if (q == 0 || nsl > 1) tot[jt] = acc[jt];
+            else tot[jt] += acc[jt];
+            acc[jt] = f32x16{};
+        }
+        ++q;
+    };
     auto compute = [&](const uint8_t* buf) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -198,6 +212,7 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
         lds_barrier();           // and every wave is done with stage kt-1
         issue(prv, kt + 4);
         compute(cur);
+        fold(kt);
     };
     issue(g_sh0, kt0);
     issue(g_sh1, kt0 + 1);
@@ -231,7 +246,7 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int row = 32 * w + 8 * (v >> 2) + 4 * lh + (v & 3);
-            if (row < nrows) out[(int64_t)row * r + j] = acc[jt][v];
+            if (row < nrows) out[(int64_t)row * r + j] = tot[jt][v];
         }
     }
 }
@@ -440,19 +455,33 @@ __global__ __launch_bounds__(256) void wgrad_prep(const float* F, bf16* hi, bf16
     }
 }
 
-constexpr int kWqTile = 64 * 512;  // 64 tokens x 256 features bf16
+// NCT = 32-feature MFMA column tiles per wave: workgroups of 128 * NCT
+// features (NCT = 2: 256, NCT = 1: 128, for grids too small to fill the CUs;
+// an element's token sum does not depend on the width, so neither do the bits)
+template <int NCT>
+struct WqTile {
+    static constexpr int kCols = 128 * NCT;          // features per workgroup
+    static constexpr int kRowB = 2 * kCols;          // bytes per token row of the tile
+    static constexpr int kBytes = 64 * kRowB;        // 64 tokens
+    static constexpr int kRowsPerBlk = 1024 / kRowB; // 2 or 4 token rows per 1 KiB DMA block
+    static constexpr int kLanesPerRow = 64 / kRowsPerBlk;
+    static constexpr int kBlkPerWave = 64 / kRowsPerBlk / 4;
+    static constexpr int kStages = NCT == 2 ? 3 : 4; // LDS stages (kStages - 1 in flight)
+};
 
-template <int MAXJT>
+template <int MAXJT, int NCT>
 __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable seg, WgradPlan plan, const bf16* fhi,
                                                           const bf16* flo) {
+    using WT = WqTile<NCT>;
     constexpr int kF = 32 * MAXJT * 128;       // one of the hi / lo panels
-    constexpr int kStage = kWqTile + 2 * kF;
+    constexpr int kStage = WT::kBytes + 2 * kF;
     __shared__ __attribute__((aligned(1024))) uint8_t b0[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t b1[kStage];
     __shared__ __attribute__((aligned(1024))) uint8_t b2[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t b3[NCT == 2 ? 16 : kStage];
     const int64_t D = a.D;
     const int w = (int)blockIdx.y;
-    const int64_t c0 = (int64_t)blockIdx.x * kWgCols;  // (feature tiles fastest: a chunk's rows are read whole)
+    const int64_t c0 = (int64_t)blockIdx.x * WT::kCols;  // (feature tiles fastest: a chunk's rows are read whole)
     const int i = adapter_of_unit(plan.chunks, seg.n, w);
     const int u = w - plan.chunks.pre[i];
     const int nchunks = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
@@ -472,11 +501,13 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
         (void*)(fhi + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(flo + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
-    // activation tile: block b = 2 token rows x 512 B; lane l -> row 2b + l/32, physical chunk l%32
-    // (row % 4 = 2*(b%2) + l/32: one lane offset per block parity)
-    const int tr = l >> 5;
-    const uint32_t q_off0 = (uint32_t)(tr * D * 2) + (uint32_t)(((l & 31) ^ (tr << 2)) << 4);
-    const uint32_t q_off1 = (uint32_t)(tr * D * 2) + (uint32_t)(((l & 31) ^ ((2 + tr) << 2)) << 4);
+    // activation tile: block b = kRowsPerBlk token rows of kRowB bytes; lane l
+    // -> row RPB*b + l/(lanes per row), physical chunk l % (lanes per row),
+    // holding logical chunk physical ^ 4 (row % 4) (the layout pfrag_tr reads).
+    // With 2-row blocks the row's parity within 4 alternates with the block.
+    const int tr = l / WT::kLanesPerRow, tc = l % WT::kLanesPerRow;
+    const uint32_t q_off0 = (uint32_t)(tr * D * 2) + (uint32_t)((tc ^ (tr << 2)) << 4);
+    const uint32_t q_off1 = (uint32_t)(tr * D * 2) + (uint32_t)((tc ^ ((2 + tr) << 2)) << 4);
     // rank panels: block b = 8 rank rows x 128 B; lane l -> row 8b + l/8, physical chunk l%8
     const int r0 = l >> 3;
     const uint32_t f_row = (uint32_t)(r0 * np * 2);
@@ -484,10 +515,11 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     auto issue = [&](uint8_t* buf, int st) {
         const uint32_t oob = st < nst ? 0u : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int blk = 8 * wu + j;
-            const uint32_t vo = ((j & 1) ? q_off1 : q_off0) + (uint32_t)blk * (uint32_t)(2 * D * 2) +
-                                (uint32_t)st * (uint32_t)(64 * D * 2) + oob;
+        for (int j = 0; j < WT::kBlkPerWave; ++j) {
+            const int blk = WT::kBlkPerWave * wu + j;
+            const uint32_t vo = ((WT::kRowsPerBlk == 2 && (j & 1)) ? q_off1 : q_off0) +
+                                (uint32_t)blk * (uint32_t)(WT::kRowsPerBlk * D * 2) + (uint32_t)st * (uint32_t)(64 * D * 2) +
+                                oob;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
 #pragma unroll
@@ -495,48 +527,66 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
             const int blk = MAXJT * wu + j;
             const uint32_t vo = f_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (uint32_t)(8 * np * 2) +
                                 (uint32_t)st * 128u + oob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)(buf + kWqTile + blk * 1024), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(buf + kWqTile + kF + blk * 1024), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)(buf + WT::kBytes + blk * 1024), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(buf + WT::kBytes + kF + blk * 1024), 16, vo, 0, 0, 0);
         }
     };
-    f32x16 acc[MAXJT][2];
+    f32x16 acc[MAXJT][NCT];
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) acc[jt][0] = acc[jt][1] = f32x16{};
+    for (int jt = 0; jt < MAXJT; ++jt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[jt][ct] = f32x16{};
     auto compute = [&](const uint8_t* buf) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 qf[2];
+            bf16x8 qf[NCT];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) qf[ct] = pfrag_tr(buf, 64 * wv + 32 * ct, 16 * kk);
+            for (int ct = 0; ct < NCT; ++ct) qf[ct] = pfrag_tr<WT::kRowB>(buf, 32 * NCT * wv + 32 * ct, 16 * kk);
 #pragma unroll
             for (int jt = 0; jt < MAXJT; ++jt) {
                 if (jt >= ntj) continue;
                 const int row = 32 * jt + l32;
-                const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kWqTile + kofs128(row, 2 * kk + lh)));
-                const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kWqTile + kF + kofs128(row, 2 * kk + lh)));
+                const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + WT::kBytes + kofs128(row, 2 * kk + lh)));
+                const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + WT::kBytes + kF + kofs128(row, 2 * kk + lh)));
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < NCT; ++ct) {
                     acc[jt][ct] = mfma32x32x16(ah, qf[ct], acc[jt][ct]);
                     acc[jt][ct] = mfma32x32x16(al, qf[ct], acc[jt][ct]);
                 }
             }
         }
     };
-    constexpr int kPer = 8 + 2 * MAXJT;  // DMA loads per wave per stage
+    constexpr int kPer = WT::kBlkPerWave + 2 * MAXJT;  // DMA loads per wave per stage
+    constexpr int kAhead = WT::kStages - 1;            // stages in flight
     auto step = [&](uint8_t* cur, uint8_t* prv, int st) {
-        wait_vmcnt<kPer>();  // stage st landed, st+1 may be in flight
-        lds_barrier();       // every wave is done with stage st-1
-        issue(prv, st + 2);
+        wait_vmcnt<(kAhead - 1) * kPer>();  // stage st landed, the next kAhead-1 may be in flight
+        lds_barrier();                      // every wave is done with stage st-1
+        issue(prv, st + kAhead);
         compute(cur);
     };
-    issue(b0, 0);
-    issue(b1, 1);
-    for (int st = 0; st < nst; st += 3) {
-        step(b0, b2, st);
-        if (st + 1 >= nst) break;
-        step(b1, b0, st + 1);
-        if (st + 2 >= nst) break;
-        step(b2, b1, st + 2);
+    if constexpr (NCT == 2) {
+        issue(b0, 0);
+        issue(b1, 1);
+        for (int st = 0; st < nst; st += 3) {
+            step(b0, b2, st);
+            if (st + 1 >= nst) break;
+            step(b1, b0, st + 1);
+            if (st + 2 >= nst) break;
+            step(b2, b1, st + 2);
+        }
+    } else {
+        issue(b0, 0);
+        issue(b1, 1);
+        issue(b2, 2);
+        for (int st = 0; st < nst; st += 4) {
+            step(b0, b3, st);
+            if (st + 1 >= nst) break;
+            step(b1, b0, st + 1);
+            if (st + 2 >= nst) break;
+            step(b2, b1, st + 2);
+            if (st + 3 >= nst) break;
+            step(b3, b2, st + 3);
+        }
     }
     wait_vmcnt<0>();
 
@@ -549,8 +599,8 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     for (int jt = 0; jt < MAXJT; ++jt) {
         if (jt >= ntj) continue;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int64_t c = c0 + wv * 64 + ct * 32 + l32;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int64_t c = c0 + 32 * NCT * wv + ct * 32 + l32;
             if (c >= D) continue;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -591,7 +641,7 @@ __global__ __launch_bounds__(256) void shrink_slice_sum(ShrinkArgs a, SegTable s
     const int i = (int)blockIdx.y;
     const int64_t n = seg.off[i + 1] - seg.off[i];
     const int r = seg.rank[i];
-    const int nsl = shrink_slices(n, r, a.K, a.scratch_row);
+    const int nsl = shrink_slices(n, r, a.K, a.scratch_row, a.split_all != 0);
     if (nsl == 1) return;
     const int64_t ne = n * r;
     const float* __restrict__ part =
@@ -615,16 +665,28 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
         if (!a.scratch) a.scratch_row = 0;
         WorkMap mp;
         bool split = false;
-        int32_t items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows);
-        // 32-token tiles (one wave each) when the 128-token ones fill at most
-        // half of the CUs: four times the workgroups, same results
         int dev = 0, cus = 256;
         if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        // K slices for every adapter when the 128-token tiles number at most a
+        // quarter of the CUs (a CU's own stream of loads bounds this kernel, so
+        // few work items leave most of HBM's bandwidth unused; with more, the
+        // one-wave tiles below spread better); the K order is the same either
+        // way.  PLORA_SHRINK_SPLIT=0 or 1 forces the choice.
+        a.split_all = 0;
+        int32_t items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows, false);
+        const char* fsplit = getenv("PLORA_SHRINK_SPLIT");
+        const int fs = fsplit ? atoi(fsplit) : -1;
+        if (fs == 1 || (fs != 0 && 4 * (int64_t)items <= cus)) {
+            a.split_all = 1;
+            items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows, true);
+        }
+        // 32-token tiles (one wave each) when the 128-token grid fills at most
+        // half of the CUs: four times the workgroups, same results
         // (PLORA_SHRINK_TILE_ROWS=32 or 128 forces the tile size)
         const char* force = getenv("PLORA_SHRINK_TILE_ROWS");
         const int fr = force ? atoi(force) : 0;
         const bool small = fr == 32 || (fr != 128 && 2 * (int64_t)items <= cus);
-        if (small) items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, 32);
+        if (small) items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, 32, a.split_all != 0);
         const dim3 grid((unsigned)items), block(small ? 64 : 256);
         switch (((s.rmax + 31) / 32) * 2 + (small ? 1 : 0)) {
             case 2: hipLaunchKernelGGL((shrink_bf16_pipe<1, 4>), grid, block, 0, st, a, s, mp); break;
@@ -689,11 +751,22 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
     }
     const int32_t units = p.chunks.pre[s.n];
     if (units <= 0) return hipSuccess;
-    const dim3 grid((unsigned)p.col_tiles, (unsigned)units), block(256);
-    if (s.rmax <= 32)
-        hipLaunchKernelGGL((wgrad_bf16_pipe<1>), grid, block, 0, st, a, s, p, fhi, flo);
+    // 128-feature workgroups when the 256-feature grid would not give every CU
+    // two (PLORA_WGRAD_COLS=128 or 256 forces the width; same results)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const char* force = getenv("PLORA_WGRAD_COLS");
+    const int fc = force ? atoi(force) : 0;
+    const bool narrow = fc == 128 || (fc != 256 && (int64_t)p.col_tiles * units < 2 * (int64_t)cus);
+    const dim3 grid((unsigned)(narrow ? (a.D + 127) / 128 : p.col_tiles), (unsigned)units), block(256);
+    if (s.rmax <= 32 && narrow)
+        hipLaunchKernelGGL((wgrad_bf16_pipe<1, 1>), grid, block, 0, st, a, s, p, fhi, flo);
+    else if (s.rmax <= 32)
+        hipLaunchKernelGGL((wgrad_bf16_pipe<1, 2>), grid, block, 0, st, a, s, p, fhi, flo);
+    else if (narrow)
+        hipLaunchKernelGGL((wgrad_bf16_pipe<2, 1>), grid, block, 0, st, a, s, p, fhi, flo);
     else
-        hipLaunchKernelGGL((wgrad_bf16_pipe<2>), grid, block, 0, st, a, s, p, fhi, flo);
+        hipLaunchKernelGGL((wgrad_bf16_pipe<2, 2>), grid, block, 0, st, a, s, p, fhi, flo);
     return hipGetLastError();
 }
 

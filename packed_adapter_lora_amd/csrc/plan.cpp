@@ -84,13 +84,13 @@ int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows) {
 }
 
 int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split,
-                              int rows) {
+                              int rows, bool split_all) {
     int32_t t = 0;
     *any_split = false;
     for (int i = 0; i < s.n; ++i) {
         m->pre[i] = t;
         const int64_t ni = s.off[i + 1] - s.off[i];
-        const int sl = shrink_slices(ni, s.rank[i], K, row_bytes);
+        const int sl = shrink_slices(ni, s.rank[i], K, row_bytes, split_all);
         *any_split = *any_split || sl > 1;
         t += (int32_t)((ni + rows - 1) / rows) * sl;
     }

@@ -69,17 +69,25 @@ void build_segtable(const plora_desc* d, SegTable* s);
 // Shrink tiles: ceil(n_i / rows) per adapter.  Returns the total.
 int32_t build_shrink_map(const SegTable& s, WorkMap* m, int rows = kShrinkRows);
 
+// K order of the pipelined shrink.  Every H/G element is the sum of kShrinkSlices
+// K quarters, each accumulated in k order from zero, combined as
+// ((q0 + q1) + q2) + q3 in fp32 (K / 64 >= 4 stages; fewer stages: one
+// sequential sum).  Whether the quarters run one after another in one
+// wavefront or in four workgroups (K slices, whose fp32 partials go to the
+// adapter's own rows of the output activation, which the GEMM overwrites
+// afterwards, and are then added in slice order) therefore changes no bit, so
+// the split can follow the size of the grid.
+//
 // K slices of the pipelined shrink for adapter i (n tokens, rank r) over K:
-// an adapter with a single 128-token tile is split over kShrinkSlices
-// workgroups along K when the slices' fp32 partials (kShrinkSlices x n x r)
-// fit in its own rows of the output activation (row_bytes bytes per token;
-// 0 = no scratch), which the GEMM overwrites afterwards; the partials are then
-// added in slice order.  It depends on the adapter alone, so packed and
-// separate calls sum in the same order.
+// kShrinkSlices when the split is wanted (split_all, or a single 128-token
+// tile) and the slices' fp32 partials (kShrinkSlices x n x r) fit in the
+// adapter's rows of the scratch activation (row_bytes bytes per token; 0 = no
+// scratch), else 1.
 constexpr int kShrinkSlices = 4;
-constexpr int shrink_slices(int64_t n, int r, int64_t K, int64_t row_bytes) {
-    return (row_bytes > 0 && n >= 1 && n <= kShrinkTileRows && K % 64 == 0 && K / 64 >= 2 * kShrinkSlices &&
-            (int64_t)4 * kShrinkSlices * r <= row_bytes)
+constexpr int shrink_quarters(int64_t K) { return K / 64 >= kShrinkSlices ? kShrinkSlices : 1; }
+constexpr int shrink_slices(int64_t n, int r, int64_t K, int64_t row_bytes, bool split_all) {
+    return (row_bytes > 0 && n >= 1 && (split_all || n <= kShrinkTileRows) && K % 64 == 0 &&
+            K / 64 >= 2 * kShrinkSlices && (int64_t)4 * kShrinkSlices * r <= row_bytes)
                ? kShrinkSlices
                : 1;
 }
@@ -88,7 +96,7 @@ constexpr int shrink_slices(int64_t n, int r, int64_t K, int64_t row_bytes) {
 // per adapter.  Returns the total; *any_split tells whether a partial sum
 // pass is needed.
 int32_t build_shrink_pipe_map(const SegTable& s, WorkMap* m, int64_t K, int64_t row_bytes, bool* any_split,
-                              int rows);
+                              int rows, bool split_all);
 
 // Token-chunk size of the weight-gradient reduction over a feature width D.
 // It depends only on D, so an adapter's reduction order is the same whether

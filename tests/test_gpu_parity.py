@@ -81,8 +81,10 @@ def test_bf16_pipelined_tails_full(P, tile_p, monkeypatch):
 
 
 def test_shrink_tile_rows_bitwise_equal(P, monkeypatch):
-    """32- and 128-token shrink tiles give each token row the same MFMA sequence
-    (K slices included): equal bits in H, G and everything after them."""
+    """32- and 128-token shrink tiles, with and without K slices for every
+    adapter, give each token row the same K order (four K quarters, each
+    accumulated in order, added in order): equal bits in H, G and everything
+    after them."""
     import torch
     wl = workloads.custom(512, 768, [100, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
                           [32.0, 16.0, 8.0, 16.0, 4.0, 256.0], "bf16", seed=32, name="shrink_tiles")
@@ -91,11 +93,14 @@ def test_shrink_tile_rows_bitwise_equal(P, monkeypatch):
     dev = device_inputs(wl, inp)
     out = {}
     for rows in ("128", "32"):
-        monkeypatch.setenv("PLORA_SHRINK_TILE_ROWS", rows)
-        out[rows] = run_gpu(P, wl, dev)
+        for split in ("0", "1"):
+            monkeypatch.setenv("PLORA_SHRINK_TILE_ROWS", rows)
+            monkeypatch.setenv("PLORA_SHRINK_SPLIT", split)
+            out[rows + split] = run_gpu(P, wl, dev)
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
-    for k in ("H", "G", "Y", "dX", "dA", "dB"):
-        assert torch.equal(bits(out["128"][k]), bits(out["32"][k])), k
+    for v in ("1280", "320", "321"):
+        for k in ("H", "G", "Y", "dX", "dA", "dB"):
+            assert torch.equal(bits(out["1281"][k]), bits(out[v][k])), (v, k)
 
 
 # (384, 704): pipelined forward with a feature tail at either width (704 % 256,
@@ -396,3 +401,23 @@ def test_mixed_tile_widths_bitwise_equal(P, monkeypatch):
     for mode in ("256", "128"):
         for k in ("Y", "dX"):
             assert torch.equal(out[""][k].view(torch.int16), out[mode][k].view(torch.int16)), (mode, k)
+
+
+@pytest.mark.parametrize("d_in,d_out", [(512, 768), (4096, 1024)])
+def test_wgrad_widths_bitwise_equal(P, d_in, d_out, monkeypatch):
+    """128- and 256-feature weight-gradient workgroups give every dA/dB element
+    the same token sum (the feature tiling does not touch it): equal bits,
+    with multi-chunk adapters (partials and their reduction), a feature tail
+    and ranks up to 64 (and up to 32)."""
+    import torch
+    for ranks in ([16, 8, 64, 32, 1, 33], [16, 8, 32, 32, 1, 24]):
+        wl = workloads.custom(d_in, d_out, [1500, 0, 513, 1, 2300, 40], ranks, [32.0, 16.0, 8.0, 16.0, 4.0, 66.0],
+                              "bf16", seed=33, name="wgrad_widths")
+        log("case %s %dx%d ranks %s" % (wl.name, d_in, d_out, ranks))
+        dev = device_inputs(wl, workloads.make_inputs(wl))
+        out = {}
+        for cols in ("256", "128"):
+            monkeypatch.setenv("PLORA_WGRAD_COLS", cols)
+            out[cols] = run_gpu(P, wl, dev)
+        for k in ("dA", "dB"):
+            assert torch.equal(out["256"][k].view(torch.int32), out["128"][k].view(torch.int32)), k
