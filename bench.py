@@ -883,6 +883,8 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true", help="skip the MFMA / HBM ceiling probes")
     ap.add_argument("--no-clock", action="store_true", help="skip the power and clock record")
     ap.add_argument("--no-sweep", action="store_true", help="skip the adapter sweep of the default run")
+    ap.add_argument("--region-only", action="store_true",
+                    help="run only the warm-up and timed steps (for profiler runs: no other passes, sweep or oracle)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--plan", action="store_true",
                     help="plan a 120-job LoRA search with the packing planner (cost model fitted on the GPU)")
@@ -963,29 +965,12 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": load_traffic(dom, wl), "kernel": dom,
             "flops_per_launch": flops, "mean_launch_ms": round(kern[dom]["mean_ms"], 4)}
     whole = step_flops(wl) / sec / 1e12
-    log("step 2: the same step without per-kernel events (per-step event timings)")
-    _, per = timed_steps(stp, args.steps, 2)
-    step_ms = {"timed_region_mean": round(sec * 1e3, 4), "unprofiled": summary_ms(per)}
-    log("step 3: with L2 and the Infinity Cache flushed before every step")
-    import torch
-    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
-    _, perf = timed_steps(stp, args.steps, 2, flush=flush)
-    del flush
-    step_ms["cache_flushed"] = summary_ms(perf)
-    log("step 4: frozen path only (no adapters) on the same tokens")
-    d0 = P.Desc([0], [], [], wl.d_in, wl.d_out, wl.dtype, n_tokens=wl.T)
-    s0 = Stepper(P, d0, {k: dev[k] for k in ("X", "W", "dY")}, wl.T, wl.d_in, wl.d_out, 0)
-    _, per0 = timed_steps(s0, args.steps, 2)
-    del s0
-    frozen = summary_ms(per0)
-    overhead = {"frozen_ms_per_step": frozen["median"],
-                "lora_overhead_ms": round(step_ms["unprofiled"]["median"] - frozen["median"], 4),
-                "lora_overhead_frac": round((step_ms["unprofiled"]["median"] - frozen["median"]) /
-                                            step_ms["unprofiled"]["median"], 4)}
-    opt = None
-    if wl.n_adapters:
-        log("step 5: per-adapter AdamW on the step's gradients")
-        opt = run_adamw(P, wl, stp.d, dev, stp.dA, stp.dB, args.steps, args.warmup)
+    if args.region_only:
+        args.no_ceilings = args.no_clock = args.no_sweep = args.no_cpu = True
+    step_ms = {"timed_region_mean": round(sec * 1e3, 4)}
+    overhead, opt = None, None
+    if not args.region_only:
+        step_ms, overhead, opt = extra_passes(P, wl, stp, dev, args, sec)
     ceil = None
     if not args.no_ceilings:
         log("step 6: measured ceilings (sustained MFMA, HBM copy/read)")
@@ -1053,6 +1038,36 @@ def main():
                               "packing_gain": round(s3 / s2, 3),
                               "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in k2.items()}}),
                   flush=True)
+
+
+def extra_passes(P, wl, stp, dev, args, sec):
+    """The passes after the timed region: per-step event timings without the
+    library's per-kernel events, the same with the caches flushed, the
+    frozen path alone (LoRA overhead) and the per-adapter AdamW step."""
+    import torch
+    log("step 2: the same step without per-kernel events (per-step event timings)")
+    _, per = timed_steps(stp, args.steps, 2)
+    step_ms = {"timed_region_mean": round(sec * 1e3, 4), "unprofiled": summary_ms(per)}
+    log("step 3: with L2 and the Infinity Cache flushed before every step")
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    _, perf = timed_steps(stp, args.steps, 2, flush=flush)
+    del flush
+    step_ms["cache_flushed"] = summary_ms(perf)
+    log("step 4: frozen path only (no adapters) on the same tokens")
+    d0 = P.Desc([0], [], [], wl.d_in, wl.d_out, wl.dtype, n_tokens=wl.T)
+    s0 = Stepper(P, d0, {k: dev[k] for k in ("X", "W", "dY")}, wl.T, wl.d_in, wl.d_out, 0)
+    _, per0 = timed_steps(s0, args.steps, 2)
+    del s0
+    frozen = summary_ms(per0)
+    overhead = {"frozen_ms_per_step": frozen["median"],
+                "lora_overhead_ms": round(step_ms["unprofiled"]["median"] - frozen["median"], 4),
+                "lora_overhead_frac": round((step_ms["unprofiled"]["median"] - frozen["median"]) /
+                                            step_ms["unprofiled"]["median"], 4)}
+    opt = None
+    if wl.n_adapters:
+        log("step 5: per-adapter AdamW on the step's gradients")
+        opt = run_adamw(P, wl, stp.d, dev, stp.dA, stp.dB, args.steps, args.warmup)
+    return step_ms, overhead, opt
 
 
 def slice_inputs(dev, wl_n):
