@@ -407,6 +407,10 @@ def clock_record(stepper, seconds=3.0):
     back for about `seconds`, next to idle readings from before."""
     import threading
     import torch
+    # amd-smi's socket power is a running average: let it settle after the
+    # work that ran before
+    torch.cuda.synchronize()
+    time.sleep(3.0)
     idle = smi_sample()
     samples, stop = [], threading.Event()
 
