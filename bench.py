@@ -690,16 +690,21 @@ def run_block_bench(args):
         for pn in PROJ:
             P.plora_adamw_step(blk.desc[pn], cfg, *opt[pn], *grads[pn], dp["A"][pn], dp["B"][pn])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    class _Step:
+        pass
+    stepper = _Step()
+    stepper.step = step
+    # the timed region: no per-kernel events (they cost the GPU a few
+    # microseconds at every library call, and the block makes ~90 calls)
+    sec, per = timed_steps(stepper, args.steps, args.warmup)
+    log("per-kernel times: the same steps again with the library's per-launch events")
     P.plora_profile_reset()
     P.plora_profile_enable(True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / args.steps
+    sec_prof = (time.perf_counter() - t0) / args.steps
     P.plora_profile_enable(False)
     kern = {}
     for cls in ("gemm_fwd", "gemm_bwd", "shrink", "wgrad", "reduce", "norm", "rope", "swiglu", "add", "attn_fwd",
@@ -720,7 +725,10 @@ def run_block_bench(args):
            "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": "whole block step",
                         "flops_per_step": flops},
-           "kernels_ms_per_step": kern, "cpu_baseline": None}
+           "kernels_ms_per_step": kern, "step_ms": {"timed_region_mean": round(sec * 1e3, 4),
+                                                    "per_step_events": summary_ms(per),
+                                                    "with_per_kernel_events": round(sec_prof * 1e3, 4)},
+           "cpu_baseline": None}
     if not args.no_cpu:
         log("timing the oracle block on the host ...")
         out["cpu_baseline"] = block_cpu_baseline(hp, seg, ranks, alphas, x, dout, args.cpu_tokens)

@@ -147,10 +147,48 @@ int plora_backward_dAdB(const plora_desc* desc, const void* X, const void* dY, c
  * old + (s_i-scaled gradient of this call) in fp32, and adapters with no
  * tokens in this call are left unchanged.  This sums the micro-batches of one
  * optimizer step (gradient accumulation); the caller zeroes dA and dB, or
- * passes accumulate = 0, for the first micro-batch. */
+ * passes accumulate = 0, for the first micro-batch.  Either output may be
+ * skipped: dA = NULL (G is then not read) computes dB only, dB = NULL (H not
+ * read) dA only; not both. */
 int plora_backward_dAdB_acc(const plora_desc* desc, const void* X, const void* dY, const float* H,
                             const float* G, float* dA, float* dB, void* workspace,
                             size_t workspace_bytes, int accumulate, void* stream);
+
+/* Projections that read the same input.  In a Transformer block that carries
+ * LoRA on every projection [LLM+LoRA微调加速技术原理解析 (m.youleyou.com),
+ * 深入理解LoRA：基本原理与PEFT实现], the query, key and value projections read
+ * one activation X, and the gate and up projections another; with the same
+ * adapters (segments, ranks, alphas) on each, their shrinks H_p = X A_p and
+ * their gradients dA_p = s_i X^T G_p can share one pass over X, which is most
+ * of their memory traffic (the packed operators are tiled for memory-access
+ * efficiency [PLoRA technical summary (gist.science, arXiv 2508.02932),
+ * 方法论 > 2. LoRA 执行引擎 > 算子设计]).  np = 1, 2 or 3 projections; `desc`
+ * describes each of them (only d_in, the segments, ranks, alphas and dtype are
+ * used); A[p], H[p], G[p], dA[p] are the per-projection buffers with the
+ * layouts above (HOST arrays of np device pointers).  Every output element is
+ * bitwise the value the single-projection entry points give.
+ *
+ * plora_shrink_shared: H[p] = X A[p] (fp32, overwritten), p < np. */
+int plora_shrink_shared(const plora_desc* desc, const void* X, int np, const void* const* A, float* const* H,
+                        void* stream);
+
+/* The forward of one projection whose H was computed already (by
+ * plora_shrink_shared or plora_forward): Y = X W_m + concat_i[ s_i H_i B_i ].
+ * Y is overwritten (bitwise what plora_forward writes); H is read only. */
+int plora_forward_expand(const plora_desc* desc, const void* X, const void* W, const void* B, void* Y,
+                         const float* H, void* stream);
+
+/* dA[p]_i = s_i X[S_i]^T G[p]_i for p < np (fp32, layout of A; overwritten, or
+ * accumulated as in plora_backward_dAdB_acc).  `workspace` must hold
+ * plora_workspace_bytes_dA_shared(desc, np) bytes (NULL when that is 0); its
+ * contents on entry do not matter. */
+int plora_backward_dA_shared(const plora_desc* desc, const void* X, int np, const float* const* G,
+                             float* const* dA, void* workspace, size_t workspace_bytes, int accumulate,
+                             void* stream);
+
+/* Workspace bytes of plora_backward_dA_shared (0 for PLORA_F32, np outside
+ * 1..3 or an invalid descriptor). */
+size_t plora_workspace_bytes_dA_shared(const plora_desc* desc, int np);
 
 /* plora_backward_dAdB_acc without a workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving

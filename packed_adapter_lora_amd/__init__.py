@@ -22,6 +22,7 @@ import numpy as np
 __all__ = [
     "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
     "plora_adamw_step", "plora_cast_panels", "AdamwConfig", "plora_backward_dAdB_noalloc",
+    "plora_shrink_shared", "plora_forward_expand", "plora_backward_dA_shared", "plora_workspace_bytes_dA_shared",
     "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version", "plora_source_hash",
     "plora_profile_enable", "plora_profile_read", "plora_profile_reset", "LIB_PATH", "PLORA_F32", "PLORA_BF16",
 ]
@@ -91,6 +92,11 @@ def _load():
         "plora_backward_dAdB_acc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, ctypes.c_int,
                                                    vp]),
         "plora_backward_dAdB_noalloc": (ctypes.c_int, [dp, vp, vp, fp, fp, fp, fp, ctypes.c_int, vp]),
+        "plora_shrink_shared": (ctypes.c_int, [dp, vp, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
+        "plora_forward_expand": (ctypes.c_int, [dp, vp, vp, vp, vp, fp, vp]),
+        "plora_backward_dA_shared": (ctypes.c_int, [dp, vp, ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                                    ctypes.c_size_t, ctypes.c_int, vp]),
+        "plora_workspace_bytes_dA_shared": (ctypes.c_size_t, [dp, ctypes.c_int]),
         "plora_adamw_step": (ctypes.c_int, [dp, ctypes.POINTER(plora_adamw_config)] + [vp] * 11),
         "plora_cast_panels": (ctypes.c_int, [dp, vp, vp, vp, vp, vp]),
         "plora_rmsnorm_fwd": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_float, vp, vp, vp,
@@ -270,6 +276,59 @@ def plora_backward_dAdB_noalloc(desc: Desc, X, dY, H, G, dA, dB, accumulate=Fals
         _check_tensor(n, t, s, d)
     _check(_lib.plora_backward_dAdB_noalloc(desc.ref(), _addr(X), _addr(dY), _addr(H), _addr(G), _addr(dA),
                                             _addr(dB), 1 if accumulate else 0, _stream(stream)))
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[_addr(t) for t in ts])
+
+
+def plora_shrink_shared(desc: Desc, X, A_list, H_list, stream=None):
+    """H[p] = X A[p] for the 1-3 projections that read X (see plora.h)."""
+    T, di, R = desc.n_tokens, int(desc.c.d_in), desc.R
+    e = _elt(desc)
+    if not 1 <= len(A_list) <= 3 or len(H_list) != len(A_list):
+        raise ValueError("1 to 3 panels, one H per panel")
+    _check_tensor("X", X, (T, di), e)
+    he = plora_h_elems(desc)
+    for p, (A, H) in enumerate(zip(A_list, H_list)):
+        _check_tensor("A[%d]" % p, A, (R, di), e)
+        _check_tensor("H[%d]" % p, H, (he,), "float32")
+    _check(_lib.plora_shrink_shared(desc.ref(), _addr(X), len(A_list), _ptr_array(A_list), _ptr_array(H_list),
+                                    _stream(stream)))
+
+
+def plora_forward_expand(desc: Desc, X, W, B, Y, H, stream=None):
+    """The forward GEMM with its fused expand, H given (see plora.h)."""
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    for n, t, s_, d in (("X", X, (T, di), e), ("W", W, (do, di), e), ("B", B, (R, do), e), ("Y", Y, (T, do), e),
+                        ("H", H, (plora_h_elems(desc),), "float32")):
+        _check_tensor(n, t, s_, d)
+    _check(_lib.plora_forward_expand(desc.ref(), _addr(X), _addr(W), _addr(B), _addr(Y), _addr(H), _stream(stream)))
+
+
+def plora_workspace_bytes_dA_shared(desc: Desc, np_: int) -> int:
+    return int(_lib.plora_workspace_bytes_dA_shared(desc.ref(), int(np_)))
+
+
+def plora_backward_dA_shared(desc: Desc, X, G_list, dA_list, workspace=None, stream=None, accumulate=False):
+    """dA[p] = s_i X^T G[p] for the 1-3 projections that read X (see plora.h)."""
+    T, di, R = desc.n_tokens, int(desc.c.d_in), desc.R
+    e = _elt(desc)
+    if not 1 <= len(G_list) <= 3 or len(dA_list) != len(G_list):
+        raise ValueError("1 to 3 panels, one dA per G")
+    _check_tensor("X", X, (T, di), e)
+    he = plora_h_elems(desc)
+    for p, (G, dA) in enumerate(zip(G_list, dA_list)):
+        _check_tensor("G[%d]" % p, G, (he,), "float32")
+        _check_tensor("dA[%d]" % p, dA, (R, di), "float32")
+    nbytes = 0
+    if workspace is not None and not isinstance(workspace, int):
+        nbytes = workspace.numel() * workspace.element_size()
+    elif isinstance(workspace, int):
+        nbytes = plora_workspace_bytes_dA_shared(desc, len(G_list))
+    _check(_lib.plora_backward_dA_shared(desc.ref(), _addr(X), len(G_list), _ptr_array(G_list), _ptr_array(dA_list),
+                                         _addr(workspace), nbytes, 1 if accumulate else 0, _stream(stream)))
 
 
 class AdamwConfig:

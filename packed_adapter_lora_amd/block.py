@@ -14,15 +14,19 @@ kernels (include/plora.h, include/plora_block.h):
 
 The adapters are the same on every projection (one rank and alpha per
 adapter, as one PEFT LoRA config targets all the modules); each projection has
-its own packed A and B.
+its own packed A and B.  The projections that read one input (q, k, v from h1;
+gate and up from h2) share one pass over it for their LoRA shrinks and their
+dA gradients (plora_shrink_shared, plora_backward_dA_shared); their GEMMs and
+dB gradients run per projection.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import (Desc, plora_add, plora_attention_bwd, plora_attention_fwd, plora_backward_dAdB, plora_backward_dx,
-               plora_forward, plora_h_elems, plora_rmsnorm_bwd, plora_rmsnorm_fwd, plora_rope, plora_swiglu_bwd,
-               plora_swiglu_fwd, plora_workspace_bytes)
+from . import (Desc, plora_add, plora_attention_bwd, plora_attention_fwd, plora_backward_dA_shared,
+               plora_backward_dAdB, plora_backward_dx, plora_forward, plora_forward_expand, plora_h_elems,
+               plora_rmsnorm_bwd, plora_rmsnorm_fwd, plora_rope, plora_shrink_shared, plora_swiglu_bwd,
+               plora_swiglu_fwd, plora_workspace_bytes, plora_workspace_bytes_dA_shared)
 
 PROJ = ("q", "k", "v", "o", "g", "u", "d")
 
@@ -52,7 +56,8 @@ class DecoderBlock:
         self.dims = proj_dims(hidden, n_q, n_kv, mlp)
         self.desc = {n: Desc(self.seg, ranks, alphas, di, do, "bf16") for n, (di, do) in self.dims.items()}
         self.he = plora_h_elems(self.desc["q"])
-        nb = max(plora_workspace_bytes(d) for d in self.desc.values())
+        nb = max([plora_workspace_bytes(d) for d in self.desc.values()] +
+                 [plora_workspace_bytes_dA_shared(self.desc["q"], 3), plora_workspace_bytes_dA_shared(self.desc["g"], 2)])
         self.ws = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
         self.cache = {}
 
@@ -62,15 +67,24 @@ class DecoderBlock:
     def _f32(self, *shape):
         return self.torch.empty(shape, dtype=self.torch.float32, device="cuda")
 
+    def _shared_forward(self, names, X, c, stream):
+        """The projections `names` of one input X: one shrink pass for all
+        their H, then each projection's GEMM with its fused expand."""
+        p, T = self.p, self.T
+        for n in names:
+            c[n], c["H" + n] = self._bf(T, self.dims[n][1]), self._f32(max(self.he, 4))[:self.he]
+        if self.he:
+            plora_shrink_shared(self.desc[names[0]], X, [p["A"][n] for n in names], [c["H" + n] for n in names], stream)
+        for n in names:
+            plora_forward_expand(self.desc[n], X, p["W"][n], p["B"][n], c[n], c["H" + n], stream)
+
     def forward(self, x, stream=None):
         """x: bf16 [T, hidden].  Returns the block output; keeps what the backward needs."""
         p, T, c = self.p, self.T, {}
         c["x"] = x
         c["h1"], c["r1"] = self._bf(T, self.hidden), self._f32(T)
         plora_rmsnorm_fwd(x, p["w1"], c["h1"], c["r1"], eps=self.eps, stream=stream)
-        for n in ("q", "k", "v"):
-            c[n], c["H" + n] = self._bf(T, self.dims[n][1]), self._f32(max(self.he, 4))[:self.he]
-            plora_forward(self.desc[n], c["h1"], p["W"][n], p["A"][n], p["B"][n], c[n], c["H" + n], stream)
+        self._shared_forward(("q", "k", "v"), c["h1"], c, stream)
         plora_rope(c["q"], self.seq, self.n_q, self.base, stream=stream)  # in place: q and k are now rotated
         plora_rope(c["k"], self.seq, self.n_kv, self.base, stream=stream)
         c["att"], c["lse"] = self._bf(T, self.n_q * 128), self._f32(self.n_q, T)
@@ -79,9 +93,7 @@ class DecoderBlock:
         plora_forward(self.desc["o"], c["att"], p["W"]["o"], p["A"]["o"], p["B"]["o"], o, c["Ho"], stream)
         c["x2"], c["h2"], c["r2"] = self._bf(T, self.hidden), self._bf(T, self.hidden), self._f32(T)
         plora_rmsnorm_fwd(x, p["w2"], c["h2"], c["r2"], res=o, xs_out=c["x2"], eps=self.eps, stream=stream)
-        for n in ("g", "u"):
-            c[n], c["H" + n] = self._bf(T, self.mlp), self._f32(max(self.he, 4))[:self.he]
-            plora_forward(self.desc[n], c["h2"], p["W"][n], p["A"][n], p["B"][n], c[n], c["H" + n], stream)
+        self._shared_forward(("g", "u"), c["h2"], c, stream)
         c["a"] = self._bf(T, self.mlp)
         plora_swiglu_fwd(c["g"], c["u"], c["a"], stream)
         d, c["Hd"] = self._bf(T, self.hidden), self._f32(max(self.he, 4))[:self.he]
@@ -101,19 +113,30 @@ class DecoderBlock:
         grads = {}
         R = int(self.desc["q"].R)
 
-        def bwd(n, X, dY, H):
+        Gs = {}
+
+        def bwd(n, X, dY, H, with_dA=True):
+            """dX, G and dB of projection n (and dA unless it is left to a
+            shared pass over X)."""
             dX, G = self._bf(T, self.dims[n][0]), self._f32(max(self.he, 4))[:self.he]
             plora_backward_dx(self.desc[n], dY, p["W"][n], p["A"][n], p["B"][n], dX, G, stream)
             dA, dB = self._f32(R, self.dims[n][0]), self._f32(R, self.dims[n][1])
-            plora_backward_dAdB(self.desc[n], X, dY, H, G, dA, dB, self.ws, stream)
+            plora_backward_dAdB(self.desc[n], X if with_dA else None, dY, H, G if with_dA else None,
+                                dA if with_dA else None, dB, self.ws, stream)
             grads[n] = (dA, dB)
+            Gs[n] = G
             return dX
+
+        def shared_dA(names, X):
+            plora_backward_dA_shared(self.desc[names[0]], X, [Gs[n] for n in names], [grads[n][0] for n in names],
+                                     self.ws, stream)
 
         da = bwd("d", c["a"], dout, c["Hd"])
         dg, du = self._bf(T, self.mlp), self._bf(T, self.mlp)
         plora_swiglu_bwd(da, c["g"], c["u"], dg, du, stream)
-        dh2g = bwd("g", c["h2"], dg, c["Hg"])
-        dh2u = bwd("u", c["h2"], du, c["Hu"])
+        dh2g = bwd("g", c["h2"], dg, c["Hg"], with_dA=False)
+        dh2u = bwd("u", c["h2"], du, c["Hu"], with_dA=False)
+        shared_dA(("g", "u"), c["h2"])
         dx2 = self._bf(T, self.hidden)
         plora_rmsnorm_bwd([dh2g, dh2u], c["x2"], p["w2"], c["r2"], dx2, dres=dout, stream=stream)
         datt = bwd("o", c["att"], dx2, c["Ho"])
@@ -123,7 +146,8 @@ class DecoderBlock:
                             self.n_kv, stream)
         plora_rope(dq, self.seq, self.n_q, self.base, inverse=True, stream=stream)
         plora_rope(dk, self.seq, self.n_kv, self.base, inverse=True, stream=stream)
-        dh1 = [bwd("q", c["h1"], dq, c["Hq"]), bwd("k", c["h1"], dk, c["Hk"]), bwd("v", c["h1"], dv, c["Hv"])]
+        dh1 = [bwd(n, c["h1"], dn, c["H" + n], with_dA=False) for n, dn in (("q", dq), ("k", dk), ("v", dv))]
+        shared_dA(("q", "k", "v"), c["h1"])
         dx = self._bf(T, self.hidden)
         plora_rmsnorm_bwd(dh1, c["x"], p["w1"], c["r1"], dx, dres=dx2, stream=stream)
         if keep:

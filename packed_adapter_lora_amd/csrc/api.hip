@@ -193,8 +193,9 @@ int plora_backward_dAdB_acc(const plora_desc* d, const void* X, const void* dY, 
         int rc = check_common(d);
         if (rc) return rc;
         if (d->n_adapters == 0) return PLORA_OK;
-        if (!dA || !dB) return fail(PLORA_ERR_NULL, "dA and dB are required");
-        if (d->n_tokens > 0 && (!X || !dY || !H || !G)) return fail(PLORA_ERR_NULL, "X, dY, H and G are required");
+        if (!dA && !dB) return fail(PLORA_ERR_NULL, "dA or dB is required");
+        if (d->n_tokens > 0 && dB && (!dY || !H)) return fail(PLORA_ERR_NULL, "dB needs dY and H");
+        if (d->n_tokens > 0 && dA && (!X || !G)) return fail(PLORA_ERR_NULL, "dA needs X and G");
         if (misaligned(X) || misaligned(dY) || misaligned(H) || misaligned(G) || misaligned(dA) || misaligned(dB))
             return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
         SegTable s;
@@ -205,10 +206,14 @@ int plora_backward_dAdB_acc(const plora_desc* d, const void* X, const void* dY, 
         if (d->dtype == PLORA_F32) {
             const WgradArgs wb{dY, H, dB, nullptr, d->d_out, acc};
             const WgradArgs wa{X, G, dA, nullptr, d->d_in, acc};
-            e = timed("wgrad", st, [&] { return launch_wgrad_f32(wb, s, st); });
-            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
-            e = timed("wgrad", st, [&] { return launch_wgrad_f32(wa, s, st); });
-            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            if (dB) {
+                e = timed("wgrad", st, [&] { return launch_wgrad_f32(wb, s, st); });
+                if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            }
+            if (dA) {
+                e = timed("wgrad", st, [&] { return launch_wgrad_f32(wa, s, st); });
+                if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            }
             return PLORA_OK;
         }
         const size_t need = workspace_bytes(s, d->d_in, d->d_out);
@@ -226,11 +231,146 @@ int plora_backward_dAdB_acc(const plora_desc* d, const void* X, const void* dY, 
         __bf16* h_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_h) : nullptr;
         const WgradArgs wb{dY, H, dB, part_b, d->d_out, acc};
         const WgradArgs wa{X, G, dA, part_a, d->d_in, acc};
-        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st); });
-        if (e != hipSuccess) return hip_fail(e, "wgrad launch");
-        e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
-        if (e != hipSuccess) return hip_fail(e, "reduce launch");
-        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st); });
+        if (dB) {
+            e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st); });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
+            if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        }
+        if (dA) {
+            e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st); });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
+            if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        }
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_shrink_shared(const plora_desc* d, const void* X, int np, const void* const* A, float* const* H,
+                        void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (np < 1 || np > 3) return fail(PLORA_ERR_SHAPE, "np must be 1, 2 or 3");
+        if (d->n_adapters == 0 || d->n_tokens == 0) return PLORA_OK;
+        if (!X || !A || !H) return fail(PLORA_ERR_NULL, "X, A and H are required");
+        for (int p = 0; p < np; ++p) {
+            if (!A[p] || !H[p]) return fail(PLORA_ERR_NULL, "A[" + std::to_string(p) + "] and H[p] are required");
+            if (misaligned(A[p]) || misaligned(H[p])) return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        }
+        if (misaligned(X)) return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        hipError_t e = hipSuccess;
+        if (d->dtype == PLORA_BF16) {
+            ShrinkArgs sa{X, A[0], H[0], d->d_in, nullptr, 0, 0};
+            sa.P1 = np > 1 ? A[1] : nullptr;
+            sa.P2 = np > 2 ? A[2] : nullptr;
+            sa.out1 = np > 1 ? H[1] : nullptr;
+            sa.out2 = np > 2 ? H[2] : nullptr;
+            sa.np = np;
+            WorkMap m;
+            const int32_t units = build_shrink_map(s, &m);
+            e = timed("shrink", st, [&] { return launch_shrink_bf16(sa, s, m, units, st); });
+            if (e != hipSuccess) return hip_fail(e, "shrink launch");
+        } else {
+            for (int p = 0; p < np; ++p) {
+                const ShrinkArgs sa{X, A[p], H[p], d->d_in, nullptr, 0, 0};
+                e = timed("shrink", st, [&] { return launch_shrink_f32(sa, s, st); });
+                if (e != hipSuccess) return hip_fail(e, "shrink launch");
+            }
+        }
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_forward_expand(const plora_desc* d, const void* X, const void* W, const void* B, void* Y, const float* H,
+                         void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->n_tokens == 0) return PLORA_OK;
+        const bool lora = d->n_adapters > 0;
+        if (!X || !W || !Y) return fail(PLORA_ERR_NULL, "X, W and Y are required");
+        if (lora && (!B || !H)) return fail(PLORA_ERR_NULL, "B and H are required when n_adapters > 0");
+        if (misaligned(X) || misaligned(W) || misaligned(Y) || (lora && (misaligned(B) || misaligned(H))))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const bool bf = d->dtype == PLORA_BF16;
+        const GemmArgs ga{W, X, B, H, Y, d->n_tokens, d->d_in, d->d_out, lora ? 1 : 0};
+        const hipError_t e =
+            timed("gemm_fwd", st, [&] { return bf ? launch_gemm_bf16(true, ga, s, st) : launch_gemm_f32(true, ga, s, st); });
+        if (e != hipSuccess) return hip_fail(e, "gemm launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+size_t plora_workspace_bytes_dA_shared(const plora_desc* d, int np) {
+    if (plora_validate(d) != PLORA_OK || np < 1 || np > 3) return 0;
+    if (d->dtype == PLORA_F32) return 0;
+    SegTable s;
+    build_segtable(d, &s);
+    return dA_shared_layout(s, d->d_in, np).total;
+}
+
+int plora_backward_dA_shared(const plora_desc* d, const void* X, int np, const float* const* G, float* const* dA,
+                             void* ws, size_t ws_bytes, int accumulate, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (np < 1 || np > 3) return fail(PLORA_ERR_SHAPE, "np must be 1, 2 or 3");
+        if (d->n_adapters == 0) return PLORA_OK;
+        if (!dA || (d->n_tokens > 0 && (!X || !G))) return fail(PLORA_ERR_NULL, "X, G and dA are required");
+        for (int p = 0; p < np; ++p) {
+            if (!dA[p] || (d->n_tokens > 0 && !G[p]))
+                return fail(PLORA_ERR_NULL, "G[" + std::to_string(p) + "] and dA[p] are required");
+            if (misaligned(dA[p]) || (d->n_tokens > 0 && misaligned(G[p])))
+                return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        }
+        if (misaligned(X)) return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const int32_t acc = accumulate ? 1 : 0;
+        const float* g[3] = {nullptr, nullptr, nullptr};
+        for (int p = 0; p < np; ++p) g[p] = d->n_tokens > 0 ? G[p] : nullptr;
+        hipError_t e = hipSuccess;
+        if (d->dtype == PLORA_F32) {
+            for (int p = 0; p < np; ++p) {
+                const WgradArgs wa{X, g[p], dA[p], nullptr, d->d_in, acc};
+                e = timed("wgrad", st, [&] { return launch_wgrad_f32(wa, s, st); });
+                if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            }
+            return PLORA_OK;
+        }
+        const SharedDaLayout wl = dA_shared_layout(s, d->d_in, np);
+        if (ws_bytes < wl.total || (wl.total > 0 && !ws))
+            return fail(PLORA_ERR_WORKSPACE, "workspace needs " + std::to_string(wl.total) + " bytes");
+        if (wl.total > 0 && misaligned(ws)) return fail(PLORA_ERR_ALIGN, "workspace must be 16-byte aligned");
+        WgradPlan pa;
+        build_wgrad_plan(s, d->d_in, &pa);
+        uint8_t* wsb = static_cast<uint8_t*>(ws);
+        float* part = wsb ? reinterpret_cast<float*>(wsb) : nullptr;
+        __bf16* g_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_base) : nullptr;
+        WgradArgs wa{X, g[0], dA[0], part, d->d_in, acc};
+        wa.F1 = g[1];
+        wa.F2 = g[2];
+        wa.out1 = np > 1 ? dA[1] : nullptr;
+        wa.out2 = np > 2 ? dA[2] : nullptr;
+        wa.part_stride = (int64_t)(wl.part_stride / 4);
+        wa.ft_stride = (int64_t)(wl.ft_stride / 2);
+        wa.np = np;
+        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi ? g_hi + pa.ft_elems : nullptr, st); });
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
         e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
         if (e != hipSuccess) return hip_fail(e, "reduce launch");

@@ -105,8 +105,13 @@ __device__ __forceinline__ bf16x8 pfrag_tr(const uint8_t* tile, int p0, int kb) 
     return r;
 }
 
+// (vmcnt is 6 bits: at most 63; a wave stalls issuing beyond that, so
+// waiting for "all but the newest N" stays exact for N <= 63)
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 // workgroup barrier for LDS only: wait for this wave's LDS reads, then s_barrier
 // (no vmcnt drain, so in-flight prefetches stay in flight)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -28,6 +28,8 @@ struct GemmArgs {
 
 // Shrink: out[hoff_i + (t - o_i) r_i + j] = sum_k Q[t][k] P[R_off[i]+j][k]
 // (H = X A_i with P = A, K = d_in;  G = dY B_i^T with P = B, K = d_out).
+// Shared input: np = 2 or 3 panels P, P1, P2 (same ranks, same segments) read
+// one pass over Q and write out, out1, out2 (np = 0 or 1: P and out only).
 struct ShrinkArgs {
     const void* Q;   // [T][K]
     const void* P;   // [R][K]
@@ -36,10 +38,19 @@ struct ShrinkArgs {
     void* scratch;       // output activation (Y or dX), free until the GEMM writes it
     int64_t scratch_row; // its bytes per token row (0: no K slices)
     int32_t split_all;   // K slices for every adapter whose partials fit (not only single-tile ones)
+    const void* P1;
+    const void* P2;
+    float* out1;
+    float* out2;
+    int32_t np;
 };
 
 // Weight gradient: out[R_off[i]+j][c] = s_i sum_{t in S_i} F_i[t-o_i][j] Q[t][c]
 // (dA: F = G, Q = X, D = d_in;  dB: F = H, Q = dY, D = d_out).
+// Shared input: np = 2 or 3 factors F, F1, F2 (same ranks, same segments) and
+// outputs out, out1, out2 from one pass over Q; panel p's partials start
+// p * part_stride floats after part and its transposed hi/lo factor p *
+// ft_stride elements after the first (np = 0 or 1: F and out only).
 struct WgradArgs {
     const void* Q;     // [T][D]
     const float* F;    // H or G
@@ -47,6 +58,13 @@ struct WgradArgs {
     float* part;       // fp32 partials (adapters split over several chunks)
     int64_t D;
     int32_t accumulate;  // nonzero: out += result (adapters without tokens untouched)
+    const float* F1;
+    const float* F2;
+    float* out1;
+    float* out2;
+    int64_t part_stride;
+    int64_t ft_stride;
+    int32_t np;
 };
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);

@@ -124,16 +124,28 @@ __global__ __launch_bounds__(256) void shrink_bf16(ShrinkArgs a, SegTable seg, W
 // ---------------------------------------------------------------------------
 constexpr int kShRowB = 128;                     // bytes per LDS row (64 bf16 of k)
 
-template <int MAXJT, int WPG>
+// NP = 2 or 3: panels P, P1, P2 that share the input (the q/k/v or gate/up
+// projections of one layer) in one pass over X; each panel's accumulators see
+// the MFMA sequence of the single-panel kernel, so the bits match separate
+// calls.  Stages: as many of the 160 KiB as fit, at most five.
+template <int NP>
+__device__ __forceinline__ const void* shrink_panel(const ShrinkArgs& a, int p) {
+    return p == 0 ? a.P : p == 1 ? a.P1 : a.P2;
+}
+template <int NP>
+__device__ __forceinline__ float* shrink_out(const ShrinkArgs& a, int p) {
+    return p == 0 ? a.out : p == 1 ? a.out1 : a.out2;
+}
+
+template <int MAXJT, int WPG, int NP>
 __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, SegTable seg, WorkMap m) {
-    constexpr int TR = 32 * WPG;                           // token rows per tile
-    constexpr int kShX = TR * kShRowB;                     // token rows per stage
-    constexpr int kShStage = kShX + 32 * MAXJT * kShRowB;  // + the panel rows
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh3[kShStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh4[kShStage];
+    constexpr int TR = 32 * WPG;                                // token rows per tile
+    constexpr int kShX = TR * kShRowB;                          // token rows per stage
+    constexpr int kShPan = 32 * MAXJT * kShRowB;                // one panel's rows per stage
+    constexpr int kShStage = kShX + NP * kShPan;
+    constexpr int NST = (163840 / kShStage) < 5 ? (163840 / kShStage) : 5;  // LDS stages
+    static_assert(NST >= 3, "three stages at least");
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh[NST][kShStage];
     const int unit = (int)blockIdx.x;
     const int64_t K = a.K;
     const int i = adapter_of_unit(m, seg.n, unit);
@@ -149,16 +161,20 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
 
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(static_cast<const bf16*>(a.Q) + t0 * K), 0, (int)(nrows * K * 2), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(static_cast<const bf16*>(a.P) + (int64_t)seg.roff[i] * K), 0, (int)(r * K * 2), kRsrcWord3);
+    __amdgpu_buffer_rsrc_t ra[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        ra[p] = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(static_cast<const bf16*>(shrink_panel<NP>(a, p)) + (int64_t)seg.roff[i] * K), 0, (int)(r * K * 2),
+            kRsrcWord3);
     // DMA block b: rows 8b .. 8b+7; lane l -> row 8b + l/8, physical chunk l%8
     const int r0 = l >> 3;
     const uint32_t lane_row = (uint32_t)(r0 * K * 2);
     // this work item's stages: [kt0, kt1) of the K / 64 (one K quarter per slice)
     const int KT = (int)(K / 64), kt0 = slice * KT / nsl, kt1 = (slice + 1) * KT / nsl;
     const int nq = shrink_quarters(K);
-    // token tile: blocks 4w .. 4w+3 (32 rows per wave); panel: 4*MAXJT blocks,
-    // PB per wave
+    // token tile: blocks 4w .. 4w+3 (32 rows per wave); each panel: 4*MAXJT
+    // blocks, PB per wave
     constexpr int PB = 4 * MAXJT / WPG;
     auto issue = [&](uint8_t* buf, int kt) {
         const uint32_t oob = kt < kt1 ? 0u : 0x80000000u;
@@ -170,26 +186,38 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const int blk = PB * wu + j;
-            const uint32_t vo = lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (8u * K * 2) + kb;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + kShX + blk * 1024), 16, vo, 0, 0, 0);
+        for (int p = 0; p < NP; ++p) {
+            // (a scalar copy: an array element passed straight to the LDS DMA
+            // builtin leaves the kernel's host stub undefined)
+            const __amdgpu_buffer_rsrc_t rp = ra[p];
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+                const int blk = PB * wu + j;
+                const uint32_t vo =
+                    lane_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (8u * K * 2) + kb;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)(buf + kShX + p * kShPan + blk * 1024), 16, vo, 0,
+                                                         0, 0);
+            }
         }
     };
-    f32x16 acc[MAXJT], tot[MAXJT];
+    f32x16 acc[NP][MAXJT], tot[NP][MAXJT];
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) acc[jt] = tot[jt] = f32x16{};
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int jt = 0; jt < MAXJT; ++jt) acc[p][jt] = tot[p][jt] = f32x16{};
     int q = nsl == 1 ? 0 : slice;  // the K quarter being accumulated
     // after stage kt: at the end of quarter q, total = q0 (or this slice's
     // quarter) or total + q, and the accumulator restarts from zero
     auto fold = [&](int kt) {
         if (kt + 1 != (q + 1) * KT / nq) return;
 #pragma unroll
-        for (int jt = 0; jt < MAXJT; ++jt) {
-            if (q == 0 || nsl > 1) tot[jt] = acc[jt];
-            else tot[jt] += acc[jt];
-            acc[jt] = f32x16{};
-        }
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int jt = 0; jt < MAXJT; ++jt) {
+                if (q == 0 || nsl > 1) tot[p][jt] = acc[p][jt];
+                else tot[p][jt] += acc[p][jt];
+                acc[p][jt] = f32x16{};
+            }
         ++q;
     };
     auto compute = [&](const uint8_t* buf) {
@@ -197,56 +225,59 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
         for (int kk = 0; kk < 4; ++kk) {
             const bf16x8 xa = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kofs128(32 * w + l32, 2 * kk + lh)));
 #pragma unroll
-            for (int jt = 0; jt < MAXJT; ++jt) {
-                if (jt >= ntj) continue;
-                const bf16x8 pb = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kShX + kofs128(32 * jt + l32, 2 * kk + lh)));
-                acc[jt] = mfma32x32x16(xa, pb, acc[jt]);
-            }
+            for (int p = 0; p < NP; ++p)
+#pragma unroll
+                for (int jt = 0; jt < MAXJT; ++jt) {
+                    if (jt >= ntj) continue;
+                    const bf16x8 pb = as_bf16x8(
+                        *reinterpret_cast<const u32x4*>(buf + kShX + p * kShPan + kofs128(32 * jt + l32, 2 * kk + lh)));
+                    acc[p][jt] = mfma32x32x16(xa, pb, acc[p][jt]);
+                }
         }
     };
-    constexpr int kPer = 4 + PB;  // DMA loads per wave per stage
-    // stage kt in cur; stages kt+1 .. kt+3 in flight; refill prv (stage kt-1,
-    // done) with stage kt+4
+    constexpr int kPer = 4 + NP * PB;  // DMA loads per wave per stage
+    // stage kt in cur; stages kt+1 .. kt+NST-2 in flight; refill prv (stage
+    // kt-1, done) with stage kt+NST-1
     auto step = [&](uint8_t* cur, uint8_t* prv, int kt) {
-        wait_vmcnt<3 * kPer>();  // stage kt landed, stages kt+1 .. kt+3 may be in flight
-        lds_barrier();           // and every wave is done with stage kt-1
-        issue(prv, kt + 4);
+        // stage kt landed, the next NST-2 may be in flight (or fewer, where
+        // their loads outnumber what vmcnt can count)
+        wait_vmcnt<((NST - 2) * kPer < 63 ? (NST - 2) * kPer : 63)>();
+        lds_barrier();                   // and every wave is done with stage kt-1
+        issue(prv, kt + NST - 1);
         compute(cur);
         fold(kt);
     };
-    issue(g_sh0, kt0);
-    issue(g_sh1, kt0 + 1);
-    issue(g_sh2, kt0 + 2);
-    issue(g_sh3, kt0 + 3);
-    for (int kt = kt0; kt < kt1; kt += 5) {
-        step(g_sh0, g_sh4, kt);
-        if (kt + 1 >= kt1) break;
-        step(g_sh1, g_sh0, kt + 1);
-        if (kt + 2 >= kt1) break;
-        step(g_sh2, g_sh1, kt + 2);
-        if (kt + 3 >= kt1) break;
-        step(g_sh3, g_sh2, kt + 3);
-        if (kt + 4 >= kt1) break;
-        step(g_sh4, g_sh3, kt + 4);
+#pragma unroll
+    for (int b = 0; b < NST - 1; ++b) issue(g_sh[b], kt0 + b);
+    for (int kt = kt0; kt < kt1; kt += NST) {
+#pragma unroll
+        for (int b = 0; b < NST; ++b) {
+            if (kt + b >= kt1) break;
+            step(g_sh[b], g_sh[(b + NST - 1) % NST], kt + b);
+        }
     }
     wait_vmcnt<0>();
 
     // D[t][j]: lane holds rank column j, token rows 8*(v/4) + 4*(l/32) + v%4 of its wave's 32.
-    // K slices: slice s of the adapter's [n_i][r_i] block goes to its own rows of
-    // the scratch activation, s * n_i * r_i floats in (shrink_slice_sum adds them)
-    float* __restrict__ out =
-        (nsl == 1 ? a.out + seg.hoff[i]
-                  : reinterpret_cast<float*>(static_cast<uint8_t*>(a.scratch) + s0 * a.scratch_row) +
-                        (int64_t)slice * (s1 - s0) * r) +
-        (t0 - s0) * r;
+    // K slices (single panel only): slice s of the adapter's [n_i][r_i] block
+    // goes to its own rows of the scratch activation, s * n_i * r_i floats in
+    // (shrink_slice_sum adds them)
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) {
-        const int j = jt * 32 + l32;
-        if (jt >= ntj || j >= r) continue;
+    for (int p = 0; p < NP; ++p) {
+        float* __restrict__ out =
+            (nsl == 1 ? shrink_out<NP>(a, p) + seg.hoff[i]
+                      : reinterpret_cast<float*>(static_cast<uint8_t*>(a.scratch) + s0 * a.scratch_row) +
+                            (int64_t)slice * (s1 - s0) * r) +
+            (t0 - s0) * r;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = 32 * w + 8 * (v >> 2) + 4 * lh + (v & 3);
-            if (row < nrows) out[(int64_t)row * r + j] = tot[jt][v];
+        for (int jt = 0; jt < MAXJT; ++jt) {
+            const int j = jt * 32 + l32;
+            if (jt >= ntj || j >= r) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 32 * w + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if (row < nrows) out[(int64_t)row * r + j] = tot[p][jt][v];
+            }
         }
     }
 }
@@ -469,16 +500,33 @@ struct WqTile {
     static constexpr int kStages = NCT == 2 ? 3 : 4; // LDS stages (kStages - 1 in flight)
 };
 
-template <int MAXJT, int NCT>
+// NP = 2 or 3: factors F, F1, F2 of projections that share the input (dA of
+// the q/k/v or gate/up projections) against one pass over X; each output
+// element sees the MFMA sequence of the single-panel kernel (same bits).
+// With NP panels a 64-token stage would leave room for two stages only, so
+// these stages hold 32 tokens (rank rows of 64 bytes per hi / lo panel, 16
+// rows per DMA block) and four of them fit (three in flight); the k-steps of
+// 16 tokens and their order stay the same.
+__device__ __forceinline__ float* wgrad_out(const WgradArgs& a, int p) {
+    return p == 0 ? a.out : p == 1 ? a.out1 : a.out2;
+}
+
+template <int MAXJT, int NCT, int NP>
 __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable seg, WgradPlan plan, const bf16* fhi,
                                                           const bf16* flo) {
     using WT = WqTile<NCT>;
-    constexpr int kF = 32 * MAXJT * 128;       // one of the hi / lo panels
-    constexpr int kStage = WT::kBytes + 2 * kF;
-    __shared__ __attribute__((aligned(1024))) uint8_t b0[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t b1[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t b2[kStage];
-    __shared__ __attribute__((aligned(1024))) uint8_t b3[NCT == 2 ? 16 : kStage];
+    constexpr int TS = NP > 1 ? 32 : 64;                     // tokens per stage
+    constexpr int kXBytes = TS * WT::kRowB;                  // activation tile
+    constexpr int kXBlkPerWave = TS / WT::kRowsPerBlk / 4;   // its DMA blocks per wave
+    constexpr int kFRow = 2 * TS;                            // bytes of a rank row in one stage
+    constexpr int kF = 32 * MAXJT * kFRow;                   // one of the hi / lo panels
+    constexpr int kFBlkPerWave = NP * 2 * (kF / 1024) / 4;   // hi / lo DMA blocks per wave
+    constexpr int kStage = kXBytes + NP * 2 * kF;
+    constexpr int kMaxSt = TS == 64 ? WT::kStages : 4;
+    constexpr int NST = (163840 / kStage) < kMaxSt ? (163840 / kStage) : kMaxSt;
+    static_assert(NST >= 3, "three stages at least");
+    static_assert(NP * 2 * (kF / 1024) % 4 == 0 && MAXJT <= 2, "whole DMA blocks per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t g_b[NST][kStage];
     const int64_t D = a.D;
     const int w = (int)blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * WT::kCols;  // (feature tiles fastest: a chunk's rows are read whole)
@@ -497,10 +545,13 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
 
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(static_cast<const bf16*>(a.Q) + ta * D + c0), 0, (int)(((tb - ta - 1) * D + (D - c0)) * 2), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(fhi + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(flo + plan.ft_off[i] + (int64_t)u * TK), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
+    __amdgpu_buffer_rsrc_t rh[NP], rl[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int64_t fo = p * a.ft_stride + plan.ft_off[i] + (int64_t)u * TK;
+        rh[p] = __builtin_amdgcn_make_buffer_rsrc((void*)(fhi + fo), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
+        rl[p] = __builtin_amdgcn_make_buffer_rsrc((void*)(flo + fo), 0, (int)((r * np - (int64_t)u * TK) * 2), kRsrcWord3);
+    }
     // activation tile: block b = kRowsPerBlk token rows of kRowB bytes; lane l
     // -> row RPB*b + l/(lanes per row), physical chunk l % (lanes per row),
     // holding logical chunk physical ^ 4 (row % 4) (the layout pfrag_tr reads).
@@ -511,81 +562,101 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     // rank panels: block b = 8 rank rows x 128 B; lane l -> row 8b + l/8, physical chunk l%8
     const int r0 = l >> 3;
     const uint32_t f_row = (uint32_t)(r0 * np * 2);
-    const int nst = (int)((tb - ta + 63) / 64);
+    const int nst = (int)((tb - ta + TS - 1) / TS);
+    // 32-token stages: rank panel blocks of 16 rows x 64 B; lane l -> row 16b + l/4,
+    // physical chunk l%4, holding logical chunk (l%4) ^ (row/4 % 4) (kofs64)
+    const int r0q = l >> 2;
     auto issue = [&](uint8_t* buf, int st) {
         const uint32_t oob = st < nst ? 0u : 0x80000000u;
 #pragma unroll
-        for (int j = 0; j < WT::kBlkPerWave; ++j) {
-            const int blk = WT::kBlkPerWave * wu + j;
+        for (int j = 0; j < kXBlkPerWave; ++j) {
+            const int blk = kXBlkPerWave * wu + j;
             const uint32_t vo = ((WT::kRowsPerBlk == 2 && (j & 1)) ? q_off1 : q_off0) +
-                                (uint32_t)blk * (uint32_t)(WT::kRowsPerBlk * D * 2) + (uint32_t)st * (uint32_t)(64 * D * 2) +
+                                (uint32_t)blk * (uint32_t)(WT::kRowsPerBlk * D * 2) + (uint32_t)st * (uint32_t)(TS * D * 2) +
                                 oob;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(buf + blk * 1024), 16, vo, 0, 0, 0);
         }
+        if constexpr (TS == 64) {
 #pragma unroll
-        for (int j = 0; j < MAXJT; ++j) {
-            const int blk = MAXJT * wu + j;
-            const uint32_t vo = f_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) + (uint32_t)blk * (uint32_t)(8 * np * 2) +
-                                (uint32_t)st * 128u + oob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)(buf + WT::kBytes + blk * 1024), 16, vo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(buf + WT::kBytes + kF + blk * 1024), 16, vo, 0, 0, 0);
+            for (int p = 0; p < NP; ++p) {
+                const __amdgpu_buffer_rsrc_t rhp = rh[p], rlp = rl[p];  // (scalar copies, as in the shrink)
+#pragma unroll
+                for (int j = 0; j < MAXJT; ++j) {
+                    const int blk = MAXJT * wu + j;
+                    const uint32_t vo = f_row + (uint32_t)(((l & 7) ^ ((r0 ^ blk) & 7)) << 4) +
+                                        (uint32_t)blk * (uint32_t)(8 * np * 2) + (uint32_t)st * 128u + oob;
+                    uint8_t* fb = buf + kXBytes + p * 2 * kF;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rhp, (lds_void*)(fb + blk * 1024), 16, vo, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rlp, (lds_void*)(fb + kF + blk * 1024), 16, vo, 0, 0, 0);
+                }
+            }
+        } else {
+            // each hi / lo panel is 2 * MAXJT blocks; the panel index is fixed by
+            // j (unrolled), the block (and with MAXJT = 1 the half) by the wave
+#pragma unroll
+            for (int j = 0; j < kFBlkPerWave; ++j) {
+                const int pp = MAXJT == 2 ? j >> 1 : j;
+                const int hl = MAXJT == 2 ? (j & 1) : (wu >> 1);
+                const int b = MAXJT == 2 ? wu : (wu & 1);
+                const int row = 16 * b + r0q;
+                const uint32_t vo = (uint32_t)(row * np * 2) + (uint32_t)(((l & 3) ^ ((row >> 2) & 3)) << 4) +
+                                    (uint32_t)st * 64u + oob;
+                const __amdgpu_buffer_rsrc_t rhp = rh[pp], rlp = rl[pp];
+                const __amdgpu_buffer_rsrc_t rf = hl ? rlp : rhp;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, (lds_void*)(buf + kXBytes + (2 * pp + hl) * kF + b * 1024), 16,
+                                                         vo, 0, 0, 0);
+            }
         }
     };
-    f32x16 acc[MAXJT][NCT];
+    // logical chunk c of rank row j in a 64-byte-row panel (32-token stages)
+    auto kofs64 = [](int j, int c) { return j * 64 + ((c ^ ((j >> 2) & 3)) << 4); };
+    f32x16 acc[NP][MAXJT][NCT];
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt)
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[jt][ct] = f32x16{};
+        for (int jt = 0; jt < MAXJT; ++jt)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) acc[p][jt][ct] = f32x16{};
     auto compute = [&](const uint8_t* buf) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < TS / 16; ++kk) {
             bf16x8 qf[NCT];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) qf[ct] = pfrag_tr<WT::kRowB>(buf, 32 * NCT * wv + 32 * ct, 16 * kk);
 #pragma unroll
-            for (int jt = 0; jt < MAXJT; ++jt) {
-                if (jt >= ntj) continue;
-                const int row = 32 * jt + l32;
-                const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + WT::kBytes + kofs128(row, 2 * kk + lh)));
-                const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + WT::kBytes + kF + kofs128(row, 2 * kk + lh)));
+            for (int p = 0; p < NP; ++p)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    acc[jt][ct] = mfma32x32x16(ah, qf[ct], acc[jt][ct]);
-                    acc[jt][ct] = mfma32x32x16(al, qf[ct], acc[jt][ct]);
+                for (int jt = 0; jt < MAXJT; ++jt) {
+                    if (jt >= ntj) continue;
+                    const int row = 32 * jt + l32;
+                    const uint8_t* fb = buf + kXBytes + p * 2 * kF;
+                    const int fo = TS == 64 ? kofs128(row, 2 * kk + lh) : kofs64(row, 2 * kk + lh);
+                    const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(fb + fo));
+                    const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(fb + kF + fo));
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        acc[p][jt][ct] = mfma32x32x16(ah, qf[ct], acc[p][jt][ct]);
+                        acc[p][jt][ct] = mfma32x32x16(al, qf[ct], acc[p][jt][ct]);
+                    }
                 }
-            }
         }
     };
-    constexpr int kPer = WT::kBlkPerWave + 2 * MAXJT;  // DMA loads per wave per stage
-    constexpr int kAhead = WT::kStages - 1;            // stages in flight
+    constexpr int kPer = kXBlkPerWave + (TS == 64 ? 2 * NP * MAXJT : kFBlkPerWave);  // DMA loads per wave per stage
+    constexpr int kAhead = NST - 1;                          // stages in flight
+    constexpr int kWait = (kAhead - 1) * kPer < 63 ? (kAhead - 1) * kPer : 63;
     auto step = [&](uint8_t* cur, uint8_t* prv, int st) {
-        wait_vmcnt<(kAhead - 1) * kPer>();  // stage st landed, the next kAhead-1 may be in flight
-        lds_barrier();                      // every wave is done with stage st-1
+        wait_vmcnt<kWait>();  // stage st landed, the next kAhead-1 may be in flight
+        lds_barrier();        // every wave is done with stage st-1
         issue(prv, st + kAhead);
         compute(cur);
     };
-    if constexpr (NCT == 2) {
-        issue(b0, 0);
-        issue(b1, 1);
-        for (int st = 0; st < nst; st += 3) {
-            step(b0, b2, st);
-            if (st + 1 >= nst) break;
-            step(b1, b0, st + 1);
-            if (st + 2 >= nst) break;
-            step(b2, b1, st + 2);
-        }
-    } else {
-        issue(b0, 0);
-        issue(b1, 1);
-        issue(b2, 2);
-        for (int st = 0; st < nst; st += 4) {
-            step(b0, b3, st);
-            if (st + 1 >= nst) break;
-            step(b1, b0, st + 1);
-            if (st + 2 >= nst) break;
-            step(b2, b1, st + 2);
-            if (st + 3 >= nst) break;
-            step(b3, b2, st + 3);
+#pragma unroll
+    for (int b = 0; b < kAhead; ++b) issue(g_b[b], b);
+    for (int st = 0; st < nst; st += NST) {
+#pragma unroll
+        for (int b = 0; b < NST; ++b) {
+            if (st + b >= nst) break;
+            step(g_b[b], g_b[(b + NST - 1) % NST], st + b);
         }
     }
     wait_vmcnt<0>();
@@ -593,22 +664,25 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     // D[j][c]: lane holds feature column c, rank rows 8*(v/4) + 4*(l/32) + v%4.
     const bool direct = nchunks == 1;
     const float sc = seg.scale[i];
-    float* __restrict__ dst = direct ? a.out + (int64_t)seg.roff[i] * D
-                                     : a.part + plan.part_off[i] + (int64_t)u * r * D;
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) {
-        if (jt >= ntj) continue;
+    for (int p = 0; p < NP; ++p) {
+        float* __restrict__ dst = direct ? wgrad_out(a, p) + (int64_t)seg.roff[i] * D
+                                         : a.part + p * a.part_stride + plan.part_off[i] + (int64_t)u * r * D;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int64_t c = c0 + 32 * NCT * wv + ct * 32 + l32;
-            if (c >= D) continue;
+        for (int jt = 0; jt < MAXJT; ++jt) {
+            if (jt >= ntj) continue;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                if (j < r) {
-                    float val = direct ? sc * acc[jt][ct][v] : acc[jt][ct][v];
-                    if (direct && a.accumulate) val += dst[(int64_t)j * D + c];
-                    dst[(int64_t)j * D + c] = val;
+            for (int ct = 0; ct < NCT; ++ct) {
+                const int64_t c = c0 + 32 * NCT * wv + ct * 32 + l32;
+                if (c >= D) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int j = jt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    if (j < r) {
+                        float val = direct ? sc * acc[p][jt][ct][v] : acc[p][jt][ct][v];
+                        if (direct && a.accumulate) val += dst[(int64_t)j * D + c];
+                        dst[(int64_t)j * D + c] = val;
+                    }
                 }
             }
         }
@@ -656,13 +730,60 @@ __global__ __launch_bounds__(256) void shrink_slice_sum(ShrinkArgs a, SegTable s
 
 }  // namespace
 
+namespace {
+
+// Panel p of a shared-input call as a single-panel call.
+ShrinkArgs shrink_single(const ShrinkArgs& a, int p) {
+    ShrinkArgs o = a;
+    o.P = p == 0 ? a.P : p == 1 ? a.P1 : a.P2;
+    o.out = p == 0 ? a.out : p == 1 ? a.out1 : a.out2;
+    o.P1 = o.P2 = nullptr;
+    o.out1 = o.out2 = nullptr;
+    o.np = 1;
+    return o;
+}
+WgradArgs wgrad_single(const WgradArgs& a, int p) {
+    WgradArgs o = a;
+    o.F = p == 0 ? a.F : p == 1 ? a.F1 : a.F2;
+    o.out = p == 0 ? a.out : p == 1 ? a.out1 : a.out2;
+    o.part = a.part ? a.part + p * a.part_stride : nullptr;
+    o.F1 = o.F2 = nullptr;
+    o.out1 = o.out2 = nullptr;
+    o.np = 1;
+    return o;
+}
+
+// (kernel templates are launched from non-template code: a kernel template
+// first referenced inside a function template left its host stub undefined)
+#define PLORA_SHRINK_NP(MAXJT, WPG)                                                                          \
+    do {                                                                                                    \
+        if (np == 3)                                                                                        \
+            hipLaunchKernelGGL((shrink_bf16_pipe<MAXJT, WPG, 3>), grid, block, 0, st, a, s, mp);              \
+        else if (np == 2)                                                                                   \
+            hipLaunchKernelGGL((shrink_bf16_pipe<MAXJT, WPG, 2>), grid, block, 0, st, a, s, mp);              \
+        else                                                                                                \
+            hipLaunchKernelGGL((shrink_bf16_pipe<MAXJT, WPG, 1>), grid, block, 0, st, a, s, mp);              \
+    } while (0)
+
+}  // namespace
+
 hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st) {
     if (units <= 0) return hipSuccess;
-    if (a_in.K % 64 == 0 && (int64_t)kShrinkTileRows * a_in.K * 2 < (int64_t(1) << 31) &&
-        (int64_t)s.roff[s.n] * a_in.K * 2 < (int64_t(1) << 31)) {
+    const int np = a_in.np > 1 ? a_in.np : 1;
+    const bool pipe = a_in.K % 64 == 0 && (int64_t)kShrinkTileRows * a_in.K * 2 < (int64_t(1) << 31) &&
+                      (int64_t)s.roff[s.n] * a_in.K * 2 < (int64_t(1) << 31);
+    if (np > 1 && (!pipe || s.rmax > 64)) {
+        // shared input with ranks beyond 64 (or no pipelined shape): one pass per panel
+        for (int p = 0; p < np; ++p) {
+            const hipError_t e = launch_shrink_bf16(shrink_single(a_in, p), s, m, units, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if (pipe) {
         ShrinkArgs a = a_in;
-        if (!a.scratch) a.scratch_row = 0;
+        if (!a.scratch || np > 1) a.scratch_row = 0;  // (shared input: no K slices; the K order is the same)
         WorkMap mp;
         bool split = false;
         int dev = 0, cus = 256;
@@ -676,7 +797,7 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
         int32_t items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows, false);
         const char* fsplit = getenv("PLORA_SHRINK_SPLIT");
         const int fs = fsplit ? atoi(fsplit) : -1;
-        if (fs == 1 || (fs != 0 && 4 * (int64_t)items <= cus)) {
+        if (a.scratch_row > 0 && (fs == 1 || (fs != 0 && 4 * (int64_t)items <= cus))) {
             a.split_all = 1;
             items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, kShrinkTileRows, true);
         }
@@ -689,14 +810,14 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
         if (small) items = build_shrink_pipe_map(s, &mp, a.K, a.scratch_row, &split, 32, a.split_all != 0);
         const dim3 grid((unsigned)items), block(small ? 64 : 256);
         switch (((s.rmax + 31) / 32) * 2 + (small ? 1 : 0)) {
-            case 2: hipLaunchKernelGGL((shrink_bf16_pipe<1, 4>), grid, block, 0, st, a, s, mp); break;
-            case 3: hipLaunchKernelGGL((shrink_bf16_pipe<1, 1>), grid, block, 0, st, a, s, mp); break;
-            case 4: hipLaunchKernelGGL((shrink_bf16_pipe<2, 4>), grid, block, 0, st, a, s, mp); break;
-            case 5: hipLaunchKernelGGL((shrink_bf16_pipe<2, 1>), grid, block, 0, st, a, s, mp); break;
-            case 6: hipLaunchKernelGGL((shrink_bf16_pipe<3, 4>), grid, block, 0, st, a, s, mp); break;
-            case 7: hipLaunchKernelGGL((shrink_bf16_pipe<3, 1>), grid, block, 0, st, a, s, mp); break;
-            case 8: hipLaunchKernelGGL((shrink_bf16_pipe<4, 4>), grid, block, 0, st, a, s, mp); break;
-            default: hipLaunchKernelGGL((shrink_bf16_pipe<4, 1>), grid, block, 0, st, a, s, mp); break;
+            case 2: PLORA_SHRINK_NP(1, 4); break;
+            case 3: PLORA_SHRINK_NP(1, 1); break;
+            case 4: PLORA_SHRINK_NP(2, 4); break;
+            case 5: PLORA_SHRINK_NP(2, 1); break;
+            case 6: hipLaunchKernelGGL((shrink_bf16_pipe<3, 4, 1>), grid, block, 0, st, a, s, mp); break;
+            case 7: hipLaunchKernelGGL((shrink_bf16_pipe<3, 1, 1>), grid, block, 0, st, a, s, mp); break;
+            case 8: hipLaunchKernelGGL((shrink_bf16_pipe<4, 4, 1>), grid, block, 0, st, a, s, mp); break;
+            default: hipLaunchKernelGGL((shrink_bf16_pipe<4, 1, 1>), grid, block, 0, st, a, s, mp); break;
         }
         if (split) {
             int64_t ne = 0;  // the largest adapter's n_i * r_i: 1024 values per workgroup (at most 64 per adapter)
@@ -720,6 +841,13 @@ hipError_t launch_shrink_bf16(const ShrinkArgs& a_in, const SegTable& s, const W
 hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st) {
     const int32_t units = p.chunks.pre[s.n];
     if (units <= 0) return hipSuccess;
+    if (a.np > 1) {
+        for (int q = 0; q < a.np; ++q) {
+            const hipError_t e = launch_wgrad_bf16(wgrad_single(a, q), s, p, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     const dim3 grid((unsigned)units, (unsigned)p.col_tiles), block(256);
     const int jt = (s.rmax + 31) / 32;
     switch (jt) {
@@ -731,9 +859,20 @@ hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradP
     return hipGetLastError();
 }
 
+#define PLORA_WGRAD_NP(MAXJT, NCT)                                                                        \
+    do {                                                                                                \
+        if (np == 3)                                                                                    \
+            hipLaunchKernelGGL((wgrad_bf16_pipe<MAXJT, NCT, 3>), grid, block, 0, st, a, s, p, fhi, flo);  \
+        else if (np == 2)                                                                               \
+            hipLaunchKernelGGL((wgrad_bf16_pipe<MAXJT, NCT, 2>), grid, block, 0, st, a, s, p, fhi, flo);  \
+        else                                                                                            \
+            hipLaunchKernelGGL((wgrad_bf16_pipe<MAXJT, NCT, 1>), grid, block, 0, st, a, s, p, fhi, flo);  \
+    } while (0)
+
 hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, bf16* fhi, bf16* flo,
                                   hipStream_t st) {
     const int64_t tk = p.chunk_tokens;
+    const int np = a.np > 1 ? a.np : 1;
     // (the pipelined grid puts the chunks in y: at most 65535 of them)
     if (s.rmax > 64 || fhi == nullptr || tk * a.D * 2 >= (int64_t(1) << 31) || p.chunks.pre[s.n] > 65535)
         return launch_wgrad_bf16(a, s, p, st);
@@ -743,10 +882,13 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
         for (int i = 0; i < s.n; ++i) maxnp = maxnp > pad64(s.off[i + 1] - s.off[i]) ? maxnp : pad64(s.off[i + 1] - s.off[i]);
         if (maxnp > 0) {
             // (hi/lo offsets are multiples of 64 elements and the arrays start 16-byte aligned)
-            hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)(maxnp / 64), (unsigned)s.n), dim3(256), 0, st, a.F, fhi, flo,
-                               s, p);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
+            for (int q = 0; q < np; ++q) {
+                const float* F = q == 0 ? a.F : q == 1 ? a.F1 : a.F2;
+                hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)(maxnp / 64), (unsigned)s.n), dim3(256), 0, st, F,
+                                   fhi + q * a.ft_stride, flo + q * a.ft_stride, s, p);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
         }
     }
     const int32_t units = p.chunks.pre[s.n];
@@ -760,13 +902,13 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
     const bool narrow = fc == 128 || (fc != 256 && (int64_t)p.col_tiles * units < 2 * (int64_t)cus);
     const dim3 grid((unsigned)(narrow ? (a.D + 127) / 128 : p.col_tiles), (unsigned)units), block(256);
     if (s.rmax <= 32 && narrow)
-        hipLaunchKernelGGL((wgrad_bf16_pipe<1, 1>), grid, block, 0, st, a, s, p, fhi, flo);
+        PLORA_WGRAD_NP(1, 1);
     else if (s.rmax <= 32)
-        hipLaunchKernelGGL((wgrad_bf16_pipe<1, 2>), grid, block, 0, st, a, s, p, fhi, flo);
+        PLORA_WGRAD_NP(1, 2);
     else if (narrow)
-        hipLaunchKernelGGL((wgrad_bf16_pipe<2, 1>), grid, block, 0, st, a, s, p, fhi, flo);
+        PLORA_WGRAD_NP(2, 1);
     else
-        hipLaunchKernelGGL((wgrad_bf16_pipe<2, 2>), grid, block, 0, st, a, s, p, fhi, flo);
+        PLORA_WGRAD_NP(2, 2);
     return hipGetLastError();
 }
 
@@ -778,7 +920,13 @@ hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const Wgra
     int64_t bx = (n / 4 + 255) / 256;
     if (bx > 1024) bx = 1024;
     const dim3 grid((unsigned)bx, (unsigned)s.n), block(256);
-    hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, a, s, p);
+    const int np = a.np > 1 ? a.np : 1;
+    for (int q = 0; q < np; ++q) {
+        if (np == 1)
+            hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, a, s, p);
+        else
+            hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, wgrad_single(a, q), s, p);
+    }
     return hipGetLastError();
 }
 

@@ -142,4 +142,15 @@ size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out) {
     return workspace_layout(s, d_in, d_out).total;
 }
 
+SharedDaLayout dA_shared_layout(const SegTable& s, int64_t d_in, int np) {
+    WgradPlan a;
+    build_wgrad_plan(s, d_in, &a);
+    SharedDaLayout w;
+    w.part_stride = round256((size_t)a.part_elems * 4);
+    w.ft_base = (size_t)np * w.part_stride;
+    w.ft_stride = round256((size_t)a.ft_elems * 2 * 2);
+    w.total = w.ft_base + (size_t)np * w.ft_stride;
+    return w;
+}
+
 }  // namespace plora

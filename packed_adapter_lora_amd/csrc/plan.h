@@ -116,4 +116,12 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(const SegTable& s, int64_t d_in, int64_t d_out);
 size_t workspace_bytes(const SegTable& s, int64_t d_in, int64_t d_out);
 
+// Workspace of the shared-input dA pass over np projections: np blocks of
+// partials (part_stride bytes apart, from 0), then np hi/lo transposes of
+// the G's (ft_stride bytes apart, from ft_base).
+struct SharedDaLayout {
+    size_t part_stride, ft_base, ft_stride, total;
+};
+SharedDaLayout dA_shared_layout(const SegTable& s, int64_t d_in, int np);
+
 }  // namespace plora

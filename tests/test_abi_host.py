@@ -295,3 +295,33 @@ def test_noalloc_error_paths(P):
     assert rc == -8 and "scratch" in P.plora_last_error()
     n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
     assert lib.plora_backward_dAdB_noalloc(n0.ref(), None, None, None, None, None, None, 1, None) == 0
+
+
+def test_shared_input_error_paths(P):
+    """The shared-input entry points check the panel count, their pointers and
+    the workspace on the host before anything is enqueued; plora_backward_dAdB
+    skips a NULL output but needs one of the two."""
+    lib = P._lib
+    d = desc(P)
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    for np_ in (0, 4):
+        assert lib.plora_shrink_shared(d.ref(), 0x1000, np_, arr(0x2000), arr(0x3000), None) == -5
+        assert lib.plora_backward_dA_shared(d.ref(), 0x1000, np_, arr(0x2000), arr(0x3000), None, 0, 0, None) == -5
+        assert P.plora_workspace_bytes_dA_shared(d, np_) == 0
+    assert lib.plora_shrink_shared(d.ref(), 0x1000, 2, arr(0x2000, None), arr(0x3000, 0x4000), None) == -1
+    assert lib.plora_shrink_shared(d.ref(), 0x1000, 2, arr(0x2000, 0x2008), arr(0x3000, 0x4000), None) == -9
+    assert lib.plora_backward_dA_shared(d.ref(), 0x1000, 2, arr(0x2000, 0x2100), arr(0x3000, None), None, 0, 0,
+                                        None) == -1
+    big = desc(P, counts=(5000, 1, 0), ranks=(64, 8, 16), d_in=4096, d_out=16384)
+    need3 = P.plora_workspace_bytes_dA_shared(big, 3)
+    assert need3 > P.plora_workspace_bytes_dA_shared(big, 1) > 0
+    rc = lib.plora_backward_dA_shared(big.ref(), 0x1000, 3, arr(0x2000, 0x2100, 0x2200), arr(0x3000, 0x3100, 0x3200),
+                                      0x7000, need3 - 256, 0, None)
+    assert rc == -8 and "workspace" in P.plora_last_error()
+    assert lib.plora_forward_expand(d.ref(), 0x1000, 0x2000, None, 0x4000, 0x5000, None) == -1
+    assert lib.plora_backward_dAdB_acc(d.ref(), 0x1000, 0x2000, 0x3000, 0x4000, None, None, None, 0, 0, None) == -1
+    assert lib.plora_backward_dAdB_acc(d.ref(), 0x1000, None, 0x3000, 0x4000, None, 0x6000, None, 0, 0, None) == -1
+    # N = 0 and T = 0 are no-ops
+    n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
+    assert lib.plora_shrink_shared(n0.ref(), None, 3, None, None, None) == 0
+    assert lib.plora_backward_dA_shared(n0.ref(), None, 2, None, None, None, 0, 0, None) == 0
