@@ -145,7 +145,16 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
     constexpr int kShStage = kShX + NP * kShPan;
     constexpr int NST = (163840 / kShStage) < 5 ? (163840 / kShStage) : 5;  // LDS stages
     static_assert(NST >= 3, "three stages at least");
-    __shared__ __attribute__((aligned(1024))) uint8_t g_sh[NST][kShStage];
+    // one LDS object per stage buffer: the compiler tracks in-flight LDS DMA
+    // per object, so reads of one stage wait only for that stage's loads (one
+    // array for all stages made every LDS read wait for every load); buffers
+    // past NST are never referenced and take no LDS
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh0[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh1[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh2[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh3[kShStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_sh4[kShStage];
+    uint8_t* const g_sh[5] = {g_sh0, g_sh1, g_sh2, g_sh3, g_sh4};
     const int unit = (int)blockIdx.x;
     const int64_t K = a.K;
     const int i = adapter_of_unit(m, seg.n, unit);
@@ -526,7 +535,12 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     constexpr int NST = (163840 / kStage) < kMaxSt ? (163840 / kStage) : kMaxSt;
     static_assert(NST >= 3, "three stages at least");
     static_assert(NP * 2 * (kF / 1024) % 4 == 0 && MAXJT <= 2, "whole DMA blocks per wave");
-    __shared__ __attribute__((aligned(1024))) uint8_t g_b[NST][kStage];
+    // one LDS object per stage buffer (see the shrink); unreferenced ones take no LDS
+    __shared__ __attribute__((aligned(1024))) uint8_t g_b0[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_b1[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_b2[kStage];
+    __shared__ __attribute__((aligned(1024))) uint8_t g_b3[kStage];
+    uint8_t* const g_b[4] = {g_b0, g_b1, g_b2, g_b3};
     const int64_t D = a.D;
     const int w = (int)blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * WT::kCols;  // (feature tiles fastest: a chunk's rows are read whole)
