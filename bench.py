@@ -185,6 +185,38 @@ def rocprof_summary(trace_dir, fetch_dir, write_dir, copy_fetch_dir, copy_write_
             lines.append("%-10s %12.4g %12.4g %12.4g %10.3f %10.3f" % (cls, mean(n), c, g / 8, b / (4 * c),
                                                                         g / 8 / ns))
         out["mfma_txt"] = "\n".join(lines) + "\n"
+
+    # LDS and L2 behaviour: LDS instructions and bank-conflict cycles against the
+    # cycles the LDS was busy, the share of wave cycles spent waiting to issue an
+    # LDS instruction; L2 hit rate and the L2's read requests to the fabric (all,
+    # and those the fabric sent to DRAM)
+    lds_dir, hit_dir, ea_dir = (os.path.join(os.path.dirname(trace_dir), k) for k in ("lds", "l2hit", "l2ea"))
+    if all(os.path.isdir(x) for x in (lds_dir, hit_dir, ea_dir)):
+        cl = {c: counter(lds_dir, c) for c in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                                               "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES")}
+        ch = {c: counter(hit_dir, c) for c in ("TCC_HIT_sum", "TCC_MISS_sum")}
+        ce = {c: counter(ea_dir, c) for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_DRAM_sum")}
+        lines = ["# LDS and L2 counters per launch, workload %s" % workload,
+                 "# lds: " + cmds.get("lds", ""), "# l2 hit/miss: " + cmds.get("l2hit", ""),
+                 "# l2 fabric reads: " + cmds.get("l2ea", ""),
+                 "# conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles);"
+                 " lds_wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; l2_hit = HIT / (HIT + MISS);"
+                 " ea_rd = TCC_EA0_RDREQ_sum, of which dram = TCC_EA0_RDREQ_DRAM_sum", "",
+                 "%-10s %12s %9s %9s %8s %12s %12s" % ("class", "lds_insts", "conflict", "lds_wait", "l2_hit",
+                                                       "ea_rd", "ea_rd_dram")]
+        for name in sorted(cl["SQ_INSTS_LDS"]):
+            cls = kernel_class(name)
+            if not cls:
+                continue
+            mean = lambda d: sum(d[name]) / len(d[name]) if name in d else float("nan")
+            li, bc, ia, wl_, wc = (mean(cl[c]) for c in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                                                         "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"))
+            hit, miss = mean(ch["TCC_HIT_sum"]), mean(ch["TCC_MISS_sum"])
+            ea, dram = mean(ce["TCC_EA0_RDREQ_sum"]), mean(ce["TCC_EA0_RDREQ_DRAM_sum"])
+            lines.append("%-10s %12.4g %9.4f %9.4f %8.4f %12.4g %12.4g" % (
+                cls, li, bc / ia if ia else float("nan"), wl_ / wc if wc else float("nan"),
+                hit / (hit + miss) if hit + miss else float("nan"), ea, dram))
+        out["lds_l2_txt"] = "\n".join(lines) + "\n"
     return out
 
 
@@ -868,6 +900,9 @@ def write_profiles(d, workload):
     if "mfma_txt" in res:
         open(os.path.join(prof, "kernels_%s_mfma_clock.txt" % wl.name), "w").write(res["mfma_txt"])
         print(res["mfma_txt"])
+    if "lds_l2_txt" in res:
+        open(os.path.join(prof, "kernels_%s_lds_l2.txt" % wl.name), "w").write(res["lds_l2_txt"])
+        print(res["lds_l2_txt"])
     src = {"gemm_fwd": "gemm_bf16.hip", "gemm_bwd": "gemm_bf16.hip", "shrink": "lora_bf16.hip",
            "shrink_sum": "lora_bf16.hip", "wgrad": "lora_bf16.hip", "wgrad_prep": "lora_bf16.hip",
            "reduce": "lora_bf16.hip", "adamw": "optim.hip"}
