@@ -60,10 +60,13 @@
  * streams race, as any two kernels writing one buffer would.
  *
  * Environment.  PLORA_GEMM_TILE_P=128 or 256 forces the feature width of the
- * bf16 GEMM tiles of plora_forward / plora_backward_dx, and
- * PLORA_SHRINK_TILE_ROWS=32 or 128 the token rows of their shrink tiles (by
- * default both are chosen per shape and device).  Results are bitwise the
- * same either way.
+ * bf16 GEMM tiles of plora_forward / plora_backward_dx (by default a launch
+ * mixes 256- and 128-wide tiles by a wave count), PLORA_SHRINK_TILE_ROWS=32 or
+ * 128 the token rows of their shrink tiles, PLORA_SHRINK_SPLIT=0 or 1 whether
+ * every adapter's shrink is split along K (not only single-tile adapters),
+ * and PLORA_WGRAD_COLS=128 or 256 the feature width of the weight-gradient
+ * work items (by default all are chosen per shape and device).  Results are
+ * bitwise the same either way.
  */
 #ifndef PLORA_H
 #define PLORA_H
