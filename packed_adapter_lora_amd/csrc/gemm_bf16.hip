@@ -922,14 +922,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
             fb[s][n] = as_bf16x8(*reinterpret_cast<const u32x4*>(bt + kmaj(wq * 128 + n * 32 + l32, 2 * kk + lh)));
     };
     // serpentine order: consecutive instructions share one operand (the chip is
-    // power-capped and its clock follows how much the operands toggle); every
-    // accumulator still sees its k-steps in order, so the bits do not change
+    // power-capped and its clock follows how much the operands toggle), here
+    // the token fragment for NM instructions in a row (0.1-0.3 % faster than
+    // holding the weight fragment); every accumulator still sees its k-steps
+    // in order, so the bits do not change
     auto mm = [&](int s) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int n0 = 0; n0 < 4; ++n0) {
-                const int n = (m & 1) ? 3 - n0 : n0;
+            for (int m0 = 0; m0 < NM; ++m0) {
+                const int m = (n & 1) ? NM - 1 - m0 : m0;
                 acc[m][n] = mfma32x32x16(fa[s][m], fb[s][n], acc[m][n]);
             }
     };
