@@ -142,3 +142,45 @@ def test_shared_block_shapes_sampled(P):
     for p in range(3):
         assert torch.equal(bits(H[p]), bits(sep[p]["H"])), ("H", p)
         assert torch.equal(bits(dA[p]), bits(sep[p]["dA"])), ("dA", p)
+
+
+def random_shared_case(seed):
+    rng = np.random.default_rng(2000 + seed)
+    n = int(rng.integers(1, 10))
+    counts = [0 if rng.random() < 0.15 else int(rng.integers(1, 5)) if rng.random() < 0.3 else int(rng.integers(5, 600))
+              for _ in range(n)]
+    ranks = [int(rng.choice([1, 4, 8, 16, 24, 32, 33, 48, 64, 96, 128] if rng.random() < 0.3 else [4, 8, 16, 32, 64]))
+             for _ in range(n)]
+    alphas = [float(rng.choice([1.0, 8.0, 16.0, 32.0])) for _ in range(n)]
+    d_in = int(rng.choice([256, 512, 768])) if rng.random() < 0.7 else 8 * int(rng.integers(4, 80))
+    npan = int(rng.integers(2, 4))
+    d_outs = [int(rng.choice([128, 256, 384, 520])) for _ in range(npan)]
+    return d_in, d_outs, counts, ranks, alphas
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_shared_random_bitwise(P, seed):
+    """Randomized packings (empty and tiny segments, ranks 1..128, widths on
+    and off the tile multiples, 2 or 3 projections): the shared shrink and dA
+    equal the single-projection calls bit for bit."""
+    import torch
+    d_in, d_outs, counts, ranks, alphas = random_shared_case(seed)
+    log("case shared_random%d d_in=%d d_outs=%s counts=%s ranks=%s" % (seed, d_in, d_outs, counts, ranks))
+    wls, inps = projections(d_in, d_outs, counts, ranks, alphas, "bf16", seed=90 + seed)
+    devs = [{k: to_dev(v, "bf16") for k, v in inp.items()} for inp in inps]
+    for dv in devs[1:]:
+        dv["X"] = devs[0]["X"]
+    descs = [P.Desc.from_workload(w) for w in wls]
+    sep = [separate(P, w, dv, d) for w, dv, d in zip(wls, devs, descs)]
+    n = len(d_outs)
+    he = P.plora_h_elems(descs[0])
+    H = [poison((max(he, 1),), torch.float32)[:he] for _ in range(n)]
+    P.plora_shrink_shared(descs[0], devs[0]["X"], [dv["A"] for dv in devs], H)
+    dA = [poison((w.R, w.d_in), torch.float32) for w in wls]
+    nb = P.plora_workspace_bytes_dA_shared(descs[0], n)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    P.plora_backward_dA_shared(descs[0], devs[0]["X"], [s["G"] for s in sep], dA, ws)
+    torch.cuda.synchronize()
+    for p in range(n):
+        assert torch.equal(bits(H[p]), bits(sep[p]["H"])), ("H", p)
+        assert torch.equal(bits(dA[p]), bits(sep[p]["dA"])), ("dA", p)
