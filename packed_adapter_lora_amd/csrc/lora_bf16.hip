@@ -258,12 +258,19 @@ __global__ __launch_bounds__(64 * WPG, 1) void shrink_bf16_pipe(ShrinkArgs a, Se
     };
 #pragma unroll
     for (int b = 0; b < NST - 1; ++b) issue(g_sh[b], kt0 + b);
-    for (int kt = kt0; kt < kt1; kt += NST) {
+    // whole rotations in the loop, the rest after it: a conditional exit
+    // inside the unrolled rotation makes the compiler lose track of which
+    // buffer each in-flight load fills, and wait for all of them at the
+    // first step of every rotation
+    int kt = kt0;
+    for (; kt + NST <= kt1; kt += NST) {
 #pragma unroll
-        for (int b = 0; b < NST; ++b) {
-            if (kt + b >= kt1) break;
-            step(g_sh[b], g_sh[(b + NST - 1) % NST], kt + b);
-        }
+        for (int b = 0; b < NST; ++b) step(g_sh[b], g_sh[(b + NST - 1) % NST], kt + b);
+    }
+#pragma unroll
+    for (int b = 0; b < NST - 1; ++b) {
+        if (kt + b >= kt1) break;
+        step(g_sh[b], g_sh[(b + NST - 1) % NST], kt + b);
     }
     wait_vmcnt<0>();
 
@@ -666,12 +673,16 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
     };
 #pragma unroll
     for (int b = 0; b < kAhead; ++b) issue(g_b[b], b);
-    for (int st = 0; st < nst; st += NST) {
+    // (whole rotations in the loop, as in the shrink)
+    int st = 0;
+    for (; st + NST <= nst; st += NST) {
 #pragma unroll
-        for (int b = 0; b < NST; ++b) {
-            if (st + b >= nst) break;
-            step(g_b[b], g_b[(b + NST - 1) % NST], st + b);
-        }
+        for (int b = 0; b < NST; ++b) step(g_b[b], g_b[(b + NST - 1) % NST], st + b);
+    }
+#pragma unroll
+    for (int b = 0; b < NST - 1; ++b) {
+        if (st + b >= nst) break;
+        step(g_b[b], g_b[(b + NST - 1) % NST], st + b);
     }
     wait_vmcnt<0>();
 
