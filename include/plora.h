@@ -43,7 +43,10 @@
  *
  * Ownership and side effects.  The caller owns every buffer.  The library
  * allocates no device memory, keeps no per-call state, never synchronises and
- * enqueues work only on `stream` (a hipStream_t; NULL means the null stream).
+ * enqueues work only on `stream` (a hipStream_t; NULL means the null stream):
+ * kernels and nothing else (no memset, no copy), so a caller may capture a
+ * sequence of calls into a HIP graph and replay it; the kernel arguments,
+ * buffer addresses included, are those of the captured calls.
  * Host arrays in the descriptor are read during the call only.  Inputs are
  * never written.  Outputs (Y, H, dX, G, dA, dB) are overwritten, not
  * accumulated (plora_backward_dAdB_acc can accumulate dA and dB).  One
