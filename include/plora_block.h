@@ -34,6 +34,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "plora.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -65,6 +67,22 @@ int plora_swiglu_fwd(int64_t n, const void* g, const void* u, void* a, void* str
 
 /* dg = da * u * s * (1 + g (1 - s)), du = da * silu(g), s = sigmoid(g). */
 int plora_swiglu_bwd(int64_t n, const void* da, const void* g, const void* u, void* dg, void* du, void* stream);
+
+/* The MLP's down projection backward with the SwiGLU backward behind it:
+ * da = dY W_m^T + concat_i[ s_i G_i A_i^T ] (the packed operator's dX, as
+ * plora_backward_dx computes it [PLoRA technical summary, 方法论 › 2],
+ * rounded to bf16), then dg and du from da, g and u as plora_swiglu_bwd
+ * computes them; da itself is never stored.  desc describes the down
+ * projection (d_in = the MLP width, d_out = hidden; bf16 only, else
+ * PLORA_ERR_DTYPE); g and u [T][d_in] are the forward's gate and up
+ * activations; dg and du [T][d_in] are overwritten and must not overlap any
+ * input (dg is also the shrink's scratch, as dX is for plora_backward_dx);
+ * G as for plora_backward_dx.  dg and du are bitwise what plora_backward_dx
+ * followed by plora_swiglu_bwd writes: on shapes with the pipelined GEMM the
+ * GEMM's epilogue applies the SwiGLU backward to its rounded output, on the
+ * others the two kernels run one after the other. */
+int plora_backward_dx_swiglu(const plora_desc* desc, const void* dY, const void* W, const void* A, const void* B,
+                             const void* g, const void* u, void* dg, void* du, float* G, void* stream);
 
 /* out = x + y over n elements (n a multiple of 8); out may alias x or y. */
 int plora_add(int64_t n, const void* x, const void* y, void* out, void* stream);

@@ -21,6 +21,7 @@ import numpy as np
 
 __all__ = [
     "Desc", "PloraError", "plora_forward", "plora_backward_dx", "plora_backward_dAdB", "plora_h_elems",
+    "plora_backward_dx_swiglu",
     "plora_adamw_step", "plora_cast_panels", "AdamwConfig", "plora_backward_dAdB_noalloc",
     "plora_shrink_shared", "plora_forward_expand", "plora_backward_dA_shared", "plora_workspace_bytes_dA_shared",
     "plora_workspace_bytes", "plora_validate", "plora_status_string", "plora_last_error", "plora_version", "plora_source_hash",
@@ -106,6 +107,7 @@ def _load():
                                       vp, vp]),
         "plora_swiglu_fwd": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
         "plora_swiglu_bwd": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp, vp, vp]),
+        "plora_backward_dx_swiglu": (ctypes.c_int, [dp, vp, vp, vp, vp, vp, vp, vp, vp, fp, vp]),
         "plora_add": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
         "plora_attention_fwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 6),
         "plora_attention_bwd": (ctypes.c_int, [ctypes.c_int32, vp, ctypes.c_int32, ctypes.c_int32] + [vp] * 11),
@@ -248,6 +250,19 @@ def plora_backward_dx(desc: Desc, dY, W, A, B, dX, G, stream=None):
         _check_tensor(n, t, s, d)
     _check(_lib.plora_backward_dx(desc.ref(), _addr(dY), _addr(W), _addr(A), _addr(B), _addr(dX), _addr(G),
                                   _stream(stream)))
+
+
+def plora_backward_dx_swiglu(desc: Desc, dY, W, A, B, g, u, dg, du, G, stream=None):
+    """The down projection's dX with the SwiGLU backward applied to it: dg, du
+    (see plora_block.h); dX itself is not stored."""
+    T, di, do, R = desc.n_tokens, int(desc.c.d_in), int(desc.c.d_out), desc.R
+    e = _elt(desc)
+    for n, t, s, d in (("dY", dY, (T, do), e), ("W", W, (do, di), e), ("A", A, (R, di), e), ("B", B, (R, do), e),
+                       ("g", g, (T, di), e), ("u", u, (T, di), e), ("dg", dg, (T, di), e), ("du", du, (T, di), e),
+                       ("G", G, (plora_h_elems(desc),), "float32")):
+        _check_tensor(n, t, s, d)
+    _check(_lib.plora_backward_dx_swiglu(desc.ref(), _addr(dY), _addr(W), _addr(A), _addr(B), _addr(g), _addr(u),
+                                         _addr(dg), _addr(du), _addr(G), _stream(stream)))
 
 
 def plora_backward_dAdB(desc: Desc, X, dY, H, G, dA, dB, workspace=None, stream=None, accumulate=False):

@@ -17,15 +17,17 @@ adapter, as one PEFT LoRA config targets all the modules); each projection has
 its own packed A and B.  The projections that read one input (q, k, v from h1;
 gate and up from h2) share one pass over it for their LoRA shrinks and their
 dA gradients (plora_shrink_shared, plora_backward_dA_shared); their GEMMs and
-dB gradients run per projection.
+dB gradients run per projection.  The down projection's dX goes straight
+into the SwiGLU backward (plora_backward_dx_swiglu: its GEMM writes the
+gradients of gate and up, not dX).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from . import (Desc, plora_add, plora_attention_bwd, plora_attention_fwd, plora_backward_dA_shared,
-               plora_backward_dAdB, plora_backward_dx, plora_forward, plora_forward_expand, plora_h_elems,
-               plora_rmsnorm_bwd, plora_rmsnorm_fwd, plora_rope, plora_shrink_shared, plora_swiglu_bwd,
+               plora_backward_dAdB, plora_backward_dx, plora_backward_dx_swiglu, plora_forward, plora_forward_expand,
+               plora_h_elems, plora_rmsnorm_bwd, plora_rmsnorm_fwd, plora_rope, plora_shrink_shared,
                plora_swiglu_fwd, plora_workspace_bytes, plora_workspace_bytes_dA_shared)
 
 PROJ = ("q", "k", "v", "o", "g", "u", "d")
@@ -131,9 +133,14 @@ class DecoderBlock:
             plora_backward_dA_shared(self.desc[names[0]], X, [Gs[n] for n in names], [grads[n][0] for n in names],
                                      self.ws, stream)
 
-        da = bwd("d", c["a"], dout, c["Hd"])
-        dg, du = self._bf(T, self.mlp), self._bf(T, self.mlp)
-        plora_swiglu_bwd(da, c["g"], c["u"], dg, du, stream)
+        # down projection: its dX goes straight into the SwiGLU backward (dg, du)
+        n = "d"
+        dg, du, G = self._bf(T, self.mlp), self._bf(T, self.mlp), self._f32(max(self.he, 4))[:self.he]
+        plora_backward_dx_swiglu(self.desc[n], dout, p["W"][n], p["A"][n], p["B"][n], c["g"], c["u"], dg, du, G,
+                                 stream)
+        dA, dB = self._f32(R, self.dims[n][0]), self._f32(R, self.dims[n][1])
+        plora_backward_dAdB(self.desc[n], c["a"], dout, c["Hd"], G, dA, dB, self.ws, stream)
+        grads[n], Gs[n] = (dA, dB), G
         dh2g = bwd("g", c["h2"], dg, c["Hg"], with_dA=False)
         dh2u = bwd("u", c["h2"], du, c["Hu"], with_dA=False)
         shared_dA(("g", "u"), c["h2"])

@@ -14,9 +14,11 @@
 #include <vector>
 
 #include "api_util.h"
+#include "block_launch.h"
 #include "launch.h"
 #include "plan.h"
 #include "plora.h"
+#include "plora_block.h"
 
 #ifndef PLORA_SOURCE_HASH
 #define PLORA_SOURCE_HASH "unstamped"
@@ -176,6 +178,53 @@ int plora_backward_dx(const plora_desc* d, const void* dY, const void* W, const 
         const GemmArgs ga{W, dY, A, G, dX, d->n_tokens, d->d_out, d->d_in, lora ? 1 : 0};
         e = timed("gemm_bwd", st, [&] { return bf ? launch_gemm_bf16(false, ga, s, st) : launch_gemm_f32(false, ga, s, st); });
         if (e != hipSuccess) return hip_fail(e, "gemm launch");
+        return PLORA_OK;
+    } catch (...) {
+        return fail(PLORA_ERR_HIP, "unexpected exception");
+    }
+}
+
+int plora_backward_dx_swiglu(const plora_desc* d, const void* dY, const void* W, const void* A, const void* B,
+                             const void* g, const void* u, void* dg, void* du, float* G, void* stream) {
+    try {
+        int rc = check_common(d);
+        if (rc) return rc;
+        if (d->dtype != PLORA_BF16) return fail(PLORA_ERR_DTYPE, "the fused SwiGLU backward is bf16 only");
+        if (d->n_tokens == 0) return PLORA_OK;
+        const bool lora = d->n_adapters > 0;
+        if (!dY || !W || !g || !u || !dg || !du) return fail(PLORA_ERR_NULL, "dY, W, g, u, dg and du are required");
+        if (lora && (!A || !B || !G)) return fail(PLORA_ERR_NULL, "A, B and G are required when n_adapters > 0");
+        if (misaligned(dY) || misaligned(W) || misaligned(g) || misaligned(u) || misaligned(dg) || misaligned(du) ||
+            (lora && (misaligned(A) || misaligned(B) || misaligned(G))))
+            return fail(PLORA_ERR_ALIGN, "device pointers must be 16-byte aligned");
+        SegTable s;
+        build_segtable(d, &s);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        hipError_t e = hipSuccess;
+        if (lora) {
+            // dg is the scratch of the shrink's K slices (the GEMM writes it afterwards)
+            const ShrinkArgs sa{dY, B, G, d->d_out, dg, d->d_in * 2, 0};
+            WorkMap m;
+            const int32_t units = build_shrink_map(s, &m);
+            e = timed("shrink", st, [&] { return launch_shrink_bf16(sa, s, m, units, st); });
+            if (e != hipSuccess) return hip_fail(e, "shrink launch");
+        }
+        GemmArgs ga{W, dY, A, G, dg, d->n_tokens, d->d_out, d->d_in, lora ? 1 : 0};
+        if (gemm_bf16_pipelined(ga, s)) {
+            // da never leaves the GEMM: its epilogue writes dg and du
+            ga.sw_g = g;
+            ga.sw_u = u;
+            ga.sw_dg = dg;
+            ga.sw_du = du;
+            e = timed("gemm_bwd", st, [&] { return launch_gemm_bf16(false, ga, s, st); });
+            if (e != hipSuccess) return hip_fail(e, "gemm launch");
+        } else {
+            // da into dg, then the SwiGLU backward in place (element by element)
+            e = timed("gemm_bwd", st, [&] { return launch_gemm_bf16(false, ga, s, st); });
+            if (e != hipSuccess) return hip_fail(e, "gemm launch");
+            e = timed("swiglu", st, [&] { return launch_swiglu_bwd(dg, g, u, dg, du, d->n_tokens * d->d_in, st); });
+            if (e != hipSuccess) return hip_fail(e, "swiglu launch");
+        }
         return PLORA_OK;
     } catch (...) {
         return fail(PLORA_ERR_HIP, "unexpected exception");

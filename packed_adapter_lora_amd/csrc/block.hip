@@ -206,11 +206,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const bf16* da, const b
     load8(g + e, gv);
     load8(u + e, uv);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float s = sigmoidf(gv[k]);
-        og[k] = av[k] * uv[k] * s * (1.0f + gv[k] * (1.0f - s));
-        ou[k] = av[k] * gv[k] * s;
-    }
+    for (int k = 0; k < 8; ++k) swiglu_grad(av[k], gv[k], uv[k], og[k], ou[k]);
     store8(dg + e, og);
     store8(du + e, ou);
 }

@@ -35,6 +35,16 @@ __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(
 // Round fp32 to bf16 (nearest, ties to even; gfx950 converts in hardware).
 __device__ __forceinline__ bf16 to_bf16(float f) { return static_cast<bf16>(f); }
 
+// SwiGLU a = silu(g) * u: the gradients of g and u for one element given da,
+// s = sigmoid(g).  One definition for every kernel that applies it (the
+// SwiGLU backward kernel and the dX GEMM's fused epilogue), so both give the
+// same bits.
+__device__ __forceinline__ void swiglu_grad(float da, float g, float u, float& dg, float& du) {
+    const float s = 1.0f / (1.0f + __expf(-g));
+    dg = da * u * s * (1.0f + g * (1.0f - s));
+    du = da * g * s;
+}
+
 // Two-term bf16 split of an fp32 value: v ~= hi + lo with |v - hi - lo| <= 2^-16 |v|.
 __device__ __forceinline__ void split_bf16(float v, bf16& hi, bf16& lo) {
     hi = static_cast<bf16>(v);

@@ -230,15 +230,38 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Gemm
 // (token rows of 64*NM bytes, NS = 8*NM slots of 8 bytes); slot s of row q is
 // stored at slot s ^ (q % NS), which keeps the 8-byte writes (rows x one slot)
 // and the 16-byte reads (one row, NS/2 chunks) free of bank conflicts.  No
-// workgroup barrier: a wave only reads what it wrote.
-template <int NM = 4>
+// workgroup barrier: a wave only reads what it wrote.  SWI: the row pieces
+// are SwiGLU's da; the g and u pieces at the same place are read (eight row
+// pieces' loads issued together) and dg, du written in place of O.
+template <int NM = 4, bool SWI = false>
 __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[NM][4], const GemmArgs& a, int64_t q0, int64_t p0,
                                                uint8_t* sb) {
     constexpr int NS = 8 * NM, RB = 8 * NS, CH = NS / 2, RPI = 64 / CH;  // slots, row bytes, chunks, rows/instr
+    constexpr int NIT = 128 / RPI;                                         // row-piece stores per lane
     bf16* __restrict__ O = static_cast<bf16*>(a.O);
     const int64_t T = a.T, Pdim = a.Pdim;
     const int l = lane_id(), w = wave_id();
     const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
+    const int k = l % CH;
+    const int64_t pc = p0 + wp * (32 * NM) + 8 * k;
+    // SWI: the g and u pieces of 8 row pieces per batch, two batches in
+    // flight (rows past T and columns past Pdim load a valid piece instead;
+    // their results are not stored)
+    constexpr int BT = 8, NB = NIT / BT;
+    u32x4 gv[2][BT], uv[2][BT];
+    auto load_batch = [&](int b, int sl) {
+        const bf16* __restrict__ gp = static_cast<const bf16*>(a.sw_g);
+        const bf16* __restrict__ up = static_cast<const bf16*>(a.sw_u);
+        const int64_t pcc = pc < Pdim ? pc : Pdim - 8;
+#pragma unroll
+        for (int j = 0; j < BT; ++j) {
+            const int64_t t = q0 + wq * 128 + (b * BT + j) * RPI + l / CH;
+            const int64_t e = (t < T ? t : T - 1) * Pdim + pcc;
+            gv[sl][j] = *reinterpret_cast<const u32x4*>(gp + e);
+            uv[sl][j] = *reinterpret_cast<const u32x4*>(up + e);
+        }
+    };
+    if constexpr (SWI) load_batch(0, 0);  // (in flight during the staging writes)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
         const int q = nt * 32 + l32;
@@ -256,16 +279,47 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[NM][4], const
             }
         }
     }
-    const int k = l % CH;
-    const int64_t pc = p0 + wp * (32 * NM) + 8 * k;
+    if constexpr (SWI) {
+        bf16* __restrict__ dgp = static_cast<bf16*>(a.sw_dg);
+        bf16* __restrict__ dup = static_cast<bf16*>(a.sw_du);
+        // bf16 element e of a 16-byte piece, as fp32
+        auto elt = [](const u32x4& v, int e) {
+            return __builtin_bit_cast(float, (v[e >> 1] >> (16 * (e & 1))) << 16);
+        };
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (b + 1 < NB) load_batch(b + 1, (b + 1) & 1);
+#pragma unroll
+            for (int j = 0; j < BT; ++j) {
+                const int row = (b * BT + j) * RPI + l / CH;
+                const int x = row & (NS - 1);
+                u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * RB + ((k ^ (x >> 1)) << 4));
+                if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+                bf16x8 og, ou;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float dg, du;
+                    swiglu_grad(elt(v, e), elt(gv[b & 1][j], e), elt(uv[b & 1][j], e), dg, du);
+                    og[e] = to_bf16(dg);
+                    ou[e] = to_bf16(du);
+                }
+                const int64_t t = q0 + wq * 128 + row;
+                if (t < T && pc < Pdim) {
+                    *reinterpret_cast<u32x4*>(dgp + t * Pdim + pc) = as_u32x4(og);
+                    *reinterpret_cast<u32x4*>(dup + t * Pdim + pc) = as_u32x4(ou);
+                }
+            }
+        }
+    } else {
 #pragma unroll 4
-    for (int it = 0; it < 128 / RPI; ++it) {
-        const int row = it * RPI + l / CH;
-        const int x = row & (NS - 1);
-        u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * RB + ((k ^ (x >> 1)) << 4));
-        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int64_t t = q0 + wq * 128 + row;
-        if (t < T && pc < Pdim) *reinterpret_cast<u32x4*>(O + t * Pdim + pc) = v;
+        for (int it = 0; it < NIT; ++it) {
+            const int row = it * RPI + l / CH;
+            const int x = row & (NS - 1);
+            u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * RB + ((k ^ (x >> 1)) << 4));
+            if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+            const int64_t t = q0 + wq * 128 + row;
+            if (t < T && pc < Pdim) *reinterpret_cast<u32x4*>(O + t * Pdim + pc) = v;
+        }
     }
 }
 
@@ -833,7 +887,7 @@ __device__ __forceinline__ void lora_expand_pipe(f32x16 (&acc)[NM][4], const Gem
 // NM = 32-feature MFMA blocks per wave: tiles of 64*NM features x 256 tokens
 // (NM = 4: 256 x 256; NM = 2: 128 x 256, twice the tiles for shapes whose
 // 256-wide tiles leave most of the chip idle or a last partial wave).
-template <bool P_KMAJOR, int NM>
+template <bool P_KMAJOR, int NM, bool SWI = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, SegTable seg) {
     constexpr int BP = 64 * NM;          // features per tile
     constexpr int WL = 2 * NM;           // weight-tile loads per wave and stage
@@ -1001,7 +1055,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
         lora_expand_pipe<NM>(acc, a, seg, q0, p0, g_t0, g_t1, g_w0, g_w1, g_t2);
         __syncthreads();  // the expand's LDS reads are done before the staging writes
     }
-    store_tile_lds<NM>(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
+    store_tile_lds<NM, SWI>(acc, a, q0, p0, wu == 0 ? g_t0 : wu == 1 ? g_t1 : wu == 2 ? g_t2 : g_w0);
 }
 }  // namespace
 
@@ -1019,17 +1073,24 @@ static int cu_count() {
     return n;
 }
 
+// 32-bit buffer ranges: one tile's token rows (256 x K elements), the weight
+// and the expand's E rows all stay below 2^31 bytes
+bool gemm_bf16_pipelined(const GemmArgs& a, const SegTable& s) {
+    return a.K % 128 == 0 && a.K < (int64_t(1) << 22) && a.Pdim < (int64_t(1) << 22) &&
+           a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
+           (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
+}
+
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st) {
     const int64_t tq = (a.T + kBQ - 1) / kBQ, tp = (a.Pdim + kBP - 1) / kBP;
     const int64_t nwg = tq * tp;
     if (nwg <= 0) return hipSuccess;
     if (nwg > 0x3fffffff) return hipErrorInvalidValue;
     const dim3 block(kThreads);
-    // 32-bit buffer ranges: one tile's token rows (256 x K elements), the
-    // weight and the expand's E rows all stay below 2^31 bytes
-    const bool pipelined = a.K % 128 == 0 && a.K < (int64_t(1) << 22) && a.Pdim < (int64_t(1) << 22) &&
-                           a.K * a.Pdim * 2 < (int64_t(1) << 31) &&
-                           (int64_t)(s.roff[s.n] + 64) * a.Pdim * 2 < (int64_t(1) << 31);  // expand's E range
+    const bool pipelined = gemm_bf16_pipelined(a, s);
+    // the fused SwiGLU epilogue exists for the pipelined dX GEMM only
+    const bool swi = a.sw_g != nullptr;
+    if (swi && (p_kmajor || !pipelined)) return hipErrorInvalidValue;
     if (pipelined) {
         // Tile widths.  A 128-wide tile takes ~0.57 of a 256-wide tile's time.
         // All 128-wide when they fit on the chip at once (a few hundred tokens).
@@ -1065,6 +1126,8 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
             const dim3 grid((unsigned)(tq * f));
             if (p_kmajor)
                 hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 4>), grid, block, 0, st, w, s);
+            else if (swi)
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4, true>), grid, block, 0, st, w, s);
             else
                 hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4>), grid, block, 0, st, w, s);
         }
@@ -1075,6 +1138,8 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
             const dim3 grid((unsigned)(tq * ((a.Pdim - 256 * f + 127) / 128)));
             if (p_kmajor)
                 hipLaunchKernelGGL((gemm_lora_bf16_pipe<true, 2>), grid, block, 0, st, h, s);
+            else if (swi)
+                hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 2, true>), grid, block, 0, st, h, s);
             else
                 hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 2>), grid, block, 0, st, h, s);
         }

@@ -24,6 +24,13 @@ struct GemmArgs {
     // feature range [p_begin, p_end) covered by one launch of the pipelined
     // kernel (p_end = 0: up to Pdim); Pdim stays the row length and bound
     int64_t p_begin, p_end;
+    // SwiGLU backward fused into the epilogue (dX GEMM, pipelined path only;
+    // sw_g = null: plain output O): with da = O's bf16 value, writes
+    // sw_dg / sw_du [T][Pdim] from sw_g / sw_u [T][Pdim] instead of O
+    const void* sw_g;
+    const void* sw_u;
+    void* sw_dg;
+    void* sw_du;
 };
 
 // Shrink: out[hoff_i + (t - o_i) r_i + j] = sum_k Q[t][k] P[R_off[i]+j][k]
@@ -68,6 +75,9 @@ struct WgradArgs {
 };
 
 hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s, hipStream_t st);
+// whether launch_gemm_bf16 takes the pipelined kernels for this shape (the
+// only ones with the fused SwiGLU epilogue)
+bool gemm_bf16_pipelined(const GemmArgs& a, const SegTable& s);
 hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st);
 hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);

@@ -325,3 +325,25 @@ def test_shared_input_error_paths(P):
     n0 = P.Desc([0], [], [], 64, 32, "bf16", n_tokens=5)
     assert lib.plora_shrink_shared(n0.ref(), None, 3, None, None, None) == 0
     assert lib.plora_backward_dA_shared(n0.ref(), None, 2, None, None, None, 0, 0, None) == 0
+
+
+def test_dx_swiglu_error_paths(P):
+    """The fused down-projection/SwiGLU backward validates on the host: bf16
+    only, every pointer it writes or reads, 16-byte alignment; T = 0 is a
+    no-op."""
+    lib = P._lib
+    d = desc(P)
+    # pointer values that every case below rejects before anything is enqueued
+    args = [0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 0x7000, 0x8000, 0x9000]
+    f32 = desc(P, dtype="f32")
+    assert lib.plora_backward_dx_swiglu(f32.ref(), *args, None) == -7
+    for k in (0, 1, 4, 5, 6, 7):  # dY, W, g, u, dg, du
+        a = list(args)
+        a[k] = None
+        assert lib.plora_backward_dx_swiglu(d.ref(), *a, None) == -1, k
+    a = list(args)
+    a[4] += 8  # g misaligned
+    assert lib.plora_backward_dx_swiglu(d.ref(), *a, None) == -9
+    assert lib.plora_backward_dx_swiglu(desc(P, ranks=(4, 0, 16)).ref(), *args, None) == -3
+    n0 = P.Desc([0, 0], [8], [16.0], 64, 32, "bf16")
+    assert lib.plora_backward_dx_swiglu(n0.ref(), *([None] * 9), None) == 0

@@ -117,6 +117,57 @@ def test_swiglu_and_add(P):
     np.testing.assert_array_equal(host(out), rnd(g.astype(np.float64) + u))
 
 
+# (768, 512): pipelined GEMM (fused epilogue) at both tile widths, a ragged
+# token tail, K-sliced shrinks (adapters of <= 128 tokens use dg as scratch);
+# (768, 264): K = 264 is off the pipelined path (GEMM, then the SwiGLU kernel
+# in place); n_adapters = 0: the frozen GEMM alone
+@pytest.mark.parametrize("d_mlp,d_hid,tile_p,frozen", [(768, 512, "256", False), (768, 512, "128", False),
+                                                       (768, 264, "256", False), (768, 512, "256", True)])
+def test_backward_dx_swiglu_fused(P, d_mlp, d_hid, tile_p, frozen, monkeypatch):
+    """plora_backward_dx_swiglu writes bitwise what plora_backward_dx followed
+    by plora_swiglu_bwd writes (dg, du and G), and the oracle's SwiGLU
+    backward of the oracle's dX within the bf16 tolerance."""
+    import torch
+    import oracle
+    from parity_utils import to_dev
+    monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
+    wl = workloads.custom(d_mlp, d_hid, [300, 0, 64, 1, 335], [16, 8, 64, 32, 1], [32.0, 16.0, 8.0, 16.0, 4.0],
+                          "bf16", seed=81, name="dx_swiglu")
+    log("case %s d_mlp=%d d_hid=%d tile_p=%s frozen=%s" % (wl.name, d_mlp, d_hid, tile_p, frozen))
+    inp = workloads.make_inputs(wl)
+    d = P.Desc([0], [], [], d_mlp, d_hid, "bf16", n_tokens=wl.T) if frozen else P.Desc.from_workload(wl)
+    T = wl.T
+    dY, W = to_dev(inp["dY"], "bf16"), to_dev(inp["W"], "bf16")
+    A = None if frozen else to_dev(inp["A"], "bf16")
+    B = None if frozen else to_dev(inp["B"], "bf16")
+    g, u = bf((T, d_mlp), 82, 1, 3.0), bf((T, d_mlp), 82, 2)
+    gd, ud = dev(g), dev(u)
+    he = P.plora_h_elems(d)
+    nan = lambda *shape: torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    G0 = torch.full((max(he, 4),), float("nan"), device="cuda")[:he] if he else None
+    G1 = torch.full((max(he, 4),), float("nan"), device="cuda")[:he] if he else None
+    dX, dg0, du0 = nan(T, d_mlp), nan(T, d_mlp), nan(T, d_mlp)
+    P.plora_backward_dx(d, dY, W, A, B, dX, G0)
+    P.plora_swiglu_bwd(dX, gd, ud, dg0, du0)
+    dg1, du1 = nan(T, d_mlp), nan(T, d_mlp)
+    P.plora_backward_dx_swiglu(d, dY, W, A, B, gd, ud, dg1, du1, G1)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16)
+    assert torch.equal(bits(dg1), bits(dg0)), "dg"
+    assert torch.equal(bits(du1), bits(du0)), "du"
+    if he:
+        assert torch.equal(G1.view(torch.int32), G0.view(torch.int32)), "G"
+    # against the oracle: its dX (fp64), rounded to bf16 as the GEMM stores it,
+    # through its SwiGLU backward
+    if frozen:
+        dx_ref = inp["dY"].astype(np.float64) @ inp["W"].astype(np.float64)
+    else:
+        dx_ref = oracle.run_workload(wl, inp)["dX"]
+    rg, ru = OB.swiglu_bwd(rnd(dx_ref), g, u)
+    check_block(host(dg1), rg, 2e-2, "dg")
+    check_block(host(du1), ru, 2e-2, "du")
+
+
 def attn_inputs(offs, n_q, n_kv, seed):
     T = offs[-1]
     return bf((T, n_q * 128), seed, 1), bf((T, n_kv * 128), seed, 2), bf((T, n_kv * 128), seed, 3)
