@@ -119,9 +119,11 @@ def test_swiglu_and_add(P):
 
 # (768, 512): pipelined GEMM (fused epilogue) at both tile widths, a ragged
 # token tail, K-sliced shrinks (adapters of <= 128 tokens use dg as scratch);
+# (712, 512): a feature tail (712 = 2 x 256 + 200) in the fused epilogue;
 # (768, 264): K = 264 is off the pipelined path (GEMM, then the SwiGLU kernel
 # in place); n_adapters = 0: the frozen GEMM alone
 @pytest.mark.parametrize("d_mlp,d_hid,tile_p,frozen", [(768, 512, "256", False), (768, 512, "128", False),
+                                                       (712, 512, "256", False), (712, 512, "128", False),
                                                        (768, 264, "256", False), (768, 512, "256", True)])
 def test_backward_dx_swiglu_fused(P, d_mlp, d_hid, tile_p, frozen, monkeypatch):
     """plora_backward_dx_swiglu writes bitwise what plora_backward_dx followed
