@@ -76,7 +76,8 @@ int plora_swiglu_bwd(int64_t n, const void* da, const void* g, const void* u, vo
  * projection (d_in = the MLP width, d_out = hidden; bf16 only, else
  * PLORA_ERR_DTYPE); g and u [T][d_in] are the forward's gate and up
  * activations; dg and du [T][d_in] are overwritten and must not overlap any
- * input (dg is also the shrink's scratch, as dX is for plora_backward_dx);
+ * input or each other (dg is also the shrink's scratch, as dX is for
+ * plora_backward_dx);
  * G as for plora_backward_dx.  dg and du are bitwise what plora_backward_dx
  * followed by plora_swiglu_bwd writes: on shapes with the pipelined GEMM the
  * GEMM's epilogue applies the SwiGLU backward to its rounded output, on the
