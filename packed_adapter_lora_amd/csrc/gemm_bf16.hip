@@ -230,7 +230,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], const Gemm
 // (token rows of 64*NM bytes, NS = 8*NM slots of 8 bytes); slot s of row q is
 // stored at slot s ^ (q % NS), which keeps the 8-byte writes (rows x one slot)
 // and the 16-byte reads (one row, NS/2 chunks) free of bank conflicts.  No
-// workgroup barrier: a wave only reads what it wrote.  SWI: the row pieces
+// workgroup barrier: a wave only reads what it wrote.  The stores are
+// non-temporal: the output is not read again by this launch, and leaving it
+// out of L2 keeps the token and weight panels there (1 % on the Y GEMM of
+// the 4096 -> 14336 shape, same bits).  SWI: the row pieces
 // are SwiGLU's da; the g and u pieces at the same place are read (eight row
 // pieces' loads issued together) and dg, du written in place of O.
 template <int NM = 4, bool SWI = false>
@@ -305,8 +308,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[NM][4], const
                 }
                 const int64_t t = q0 + wq * 128 + row;
                 if (t < T && pc < Pdim) {
-                    *reinterpret_cast<u32x4*>(dgp + t * Pdim + pc) = as_u32x4(og);
-                    *reinterpret_cast<u32x4*>(dup + t * Pdim + pc) = as_u32x4(ou);
+                    __builtin_nontemporal_store(as_u32x4(og), reinterpret_cast<u32x4*>(dgp + t * Pdim + pc));
+                    __builtin_nontemporal_store(as_u32x4(ou), reinterpret_cast<u32x4*>(dup + t * Pdim + pc));
                 }
             }
         }
@@ -318,7 +321,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[NM][4], const
             u32x4 v = *reinterpret_cast<const u32x4*>(sb + row * RB + ((k ^ (x >> 1)) << 4));
             if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
             const int64_t t = q0 + wq * 128 + row;
-            if (t < T && pc < Pdim) *reinterpret_cast<u32x4*>(O + t * Pdim + pc) = v;
+            if (t < T && pc < Pdim) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(O + t * Pdim + pc));
         }
     }
 }
