@@ -45,7 +45,6 @@ constexpr int kPRow = kBP * 2 + 16;            // bytes per p-contiguous row (pa
 constexpr int kPTile = kBK * kPRow;            // 33792 B
 constexpr int kStage = kPTile + kKTile;        // P tile (either layout) + Q tile
 constexpr int kLds = 2 * kStage;               // 132 KiB
-constexpr int kGroupQ = 2;                     // token tiles per L2 group
 
 // Byte offset of 16-byte chunk c of row r in a K-contiguous tile.  The XOR
 // keeps the 16 rows read by any 16 lanes (and any 8) on distinct bank groups.
@@ -53,18 +52,18 @@ __device__ __forceinline__ int kmaj(int r, int c) { return r * kKRow + ((c ^ ((r
 
 // Workgroup -> output tile.  Workgroups are dealt round-robin to the 8 XCDs;
 // renumber so each XCD gets a contiguous range of tiles, and walk that range
-// in groups of kGroupQ token tiles: the ~32 workgroups an XCD runs at once then
-// cover 2 token tiles x 16 feature tiles, so the two X/dY panels (2 x 2 MiB at
-// K = 4096) stay in that XCD's 4 MB L2 and the weight panels, re-read more
-// often, come from the 256 MB Infinity Cache (measured best of 1, 2, 4, 8).
-__device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_q, int tiles_p, int& tq, int& tp) {
+// in groups of gq token tiles: the ~32 workgroups an XCD runs at once then
+// cover gq token tiles x 32/gq feature tiles, so their X/dY panels stay in
+// that XCD's 4 MB L2 and the weight panels, re-read more often, come from the
+// 256 MB Infinity Cache.  The launcher picks gq (2 or 4) per shape.
+__device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_q, int tiles_p, int gq, int& tq, int& tp) {
     const int base = nwg / 8, extra = nwg % 8;
     const int xcd = bid % 8, slot = bid / 8;
     const int logical = xcd * base + (xcd < extra ? xcd : extra) + slot;
-    const int per_group = kGroupQ * tiles_p;
+    const int per_group = gq * tiles_p;
     const int group = logical / per_group;
-    const int first = group * kGroupQ;
-    const int gsize = min(tiles_q - first, kGroupQ);
+    const int first = group * gq;
+    const int gsize = min(tiles_q - first, gq);
     const int in = logical - group * per_group;
     tq = first + in % gsize;
     tp = in / gsize;
@@ -335,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16(GemmArgs a, SegTab
     const int tiles_q = (int)((T + kBQ - 1) / kBQ);
     const int tiles_p = (int)((Pdim + kBP - 1) / kBP);
     int tq, tp;
-    tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, tq, tp);
+    tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, a.group_q > 0 ? a.group_q : 2, tq, tp);
     const int64_t q0 = (int64_t)tq * kBQ, p0 = (int64_t)tp * kBP;
 
     const int tid = (int)threadIdx.x, l = lane_id(), w = wave_id();
@@ -900,7 +899,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lora_bf16_pipe(GemmArgs a, S
     const int tiles_q = (int)((T + kBQ - 1) / kBQ);
     const int tiles_p = (int)((pe - pb + BP - 1) / BP);
     int tq, tp;
-    tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, tq, tp);
+    tile_of((int)blockIdx.x, (int)gridDim.x, tiles_q, tiles_p, a.group_q > 0 ? a.group_q : 2, tq, tp);
     const int64_t q0 = (int64_t)tq * kBQ, p0 = pb + (int64_t)tp * BP;
     const int l = lane_id(), w = wave_id();
     const int wp = w & 1, wq = w >> 1, l32 = l & 31, lh = l >> 5;
@@ -1104,6 +1103,14 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
         // becomes 3 waves plus one wave of 128-wide tiles.  Each output element
         // sees the same MFMA sequence at either width, so the split does not
         // change any bit.  PLORA_GEMM_TILE_P=128 or 256 forces one width.
+        // L2 groups of 4 token tiles when K is at most 8192, else 2 (llama
+        // 4096 -> 14336: Y GEMM -0.9 % with 4, the K = 14336 dX GEMM +2.1 %;
+        // 4096 -> 4096: -1.7 % / -1.1 %).  PLORA_GEMM_GROUP_Q=2 or 4 forces it.
+        // The tile a workgroup computes changes, no output bit does.
+        GemmArgs ag = a;
+        const char* fgq = getenv("PLORA_GEMM_GROUP_Q");
+        const int fg = fgq ? atoi(fgq) : 0;
+        ag.group_q = fg == 2 || fg == 4 ? fg : (a.K <= 8192 ? 4 : 2);
         const int64_t cus = cu_count(), tp2 = (a.Pdim + 127) / 128, nwg2 = tq * tp2;
         const char* force = getenv("PLORA_GEMM_TILE_P");
         const int fw = force ? atoi(force) : 0;
@@ -1123,7 +1130,7 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
             }
         }
         if (f > 0) {
-            GemmArgs w = a;
+            GemmArgs w = ag;
             w.p_begin = 0;
             w.p_end = f == tp ? 0 : 256 * f;
             const dim3 grid((unsigned)(tq * f));
@@ -1135,7 +1142,7 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
                 hipLaunchKernelGGL((gemm_lora_bf16_pipe<false, 4>), grid, block, 0, st, w, s);
         }
         if (f < tp) {
-            GemmArgs h = a;
+            GemmArgs h = ag;
             h.p_begin = 256 * f;
             h.p_end = 0;
             const dim3 grid((unsigned)(tq * ((a.Pdim - 256 * f + 127) / 128)));

@@ -31,6 +31,7 @@ struct GemmArgs {
     const void* sw_u;
     void* sw_dg;
     void* sw_du;
+    int32_t group_q;  // token tiles per L2 group of the tile map (0: 2)
 };
 
 // Shrink: out[hoff_i + (t - o_i) r_i + j] = sum_k Q[t][k] P[R_off[i]+j][k]

@@ -107,7 +107,8 @@ def test_shrink_tile_rows_bitwise_equal(P, monkeypatch):
 # 704 % 128); (712, 640): the same for the backward GEMM (d_in = 712).
 @pytest.mark.parametrize("d_in,d_out", [(384, 704), (712, 640)])
 def test_tile_widths_bitwise_equal(P, d_in, d_out, monkeypatch):
-    """Both tile widths give every output element the same MFMA sequence: equal bits."""
+    """Both tile widths and both L2 group sizes of the tile map give every
+    output element the same MFMA sequence: equal bits."""
     import torch
     wl = workloads.custom(d_in, d_out, [100, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
                           [32.0, 16.0, 8.0, 16.0, 4.0, 256.0], "bf16", seed=31, name="tile_widths")
@@ -116,11 +117,14 @@ def test_tile_widths_bitwise_equal(P, d_in, d_out, monkeypatch):
     dev = device_inputs(wl, inp)
     out = {}
     for tile_p in ("256", "128"):
-        monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
-        out[tile_p] = run_gpu(P, wl, dev)
+        for gq in ("2", "4"):
+            monkeypatch.setenv("PLORA_GEMM_TILE_P", tile_p)
+            monkeypatch.setenv("PLORA_GEMM_GROUP_Q", gq)
+            out[tile_p + gq] = run_gpu(P, wl, dev)
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
-    for k in ("Y", "dX"):
-        assert torch.equal(bits(out["256"][k]), bits(out["128"][k])), k
+    for v in ("2564", "1282", "1284"):
+        for k in ("Y", "dX"):
+            assert torch.equal(bits(out["2562"][k]), bits(out[v][k])), (v, k)
 
 
 @TILE_WIDTHS
