@@ -68,7 +68,7 @@
  * 128 the token rows of their shrink tiles, PLORA_SHRINK_SPLIT=0 or 1 whether
  * every adapter's shrink is split along K (not only single-tile adapters),
  * PLORA_WGRAD_COLS=128 or 256 the feature width of the weight-gradient
- * work items, and PLORA_GEMM_GROUP_Q=2 or 4 the token tiles per L2 group in
+ * work items, and PLORA_GEMM_GROUP_Q=1, 2, 4 or 8 the token tiles per L2 group in
  * the GEMM's tile order (by default all are chosen per shape and device).
  * Results are bitwise the same either way.
  */

@@ -1105,12 +1105,12 @@ hipError_t launch_gemm_bf16(bool p_kmajor, const GemmArgs& a, const SegTable& s,
         // change any bit.  PLORA_GEMM_TILE_P=128 or 256 forces one width.
         // L2 groups of 4 token tiles when K is at most 8192, else 2 (llama
         // 4096 -> 14336: Y GEMM -0.9 % with 4, the K = 14336 dX GEMM +2.1 %;
-        // 4096 -> 4096: -1.7 % / -1.1 %).  PLORA_GEMM_GROUP_Q=2 or 4 forces it.
-        // The tile a workgroup computes changes, no output bit does.
+        // 4096 -> 4096: -1.7 % / -1.1 %).  PLORA_GEMM_GROUP_Q=1, 2, 4 or 8
+        // forces it.  The tile a workgroup computes changes, no output bit does.
         GemmArgs ag = a;
         const char* fgq = getenv("PLORA_GEMM_GROUP_Q");
         const int fg = fgq ? atoi(fgq) : 0;
-        ag.group_q = fg == 2 || fg == 4 ? fg : (a.K <= 8192 ? 4 : 2);
+        ag.group_q = fg == 1 || fg == 2 || fg == 4 || fg == 8 ? fg : (a.K <= 8192 ? 4 : 2);
         const int64_t cus = cu_count(), tp2 = (a.Pdim + 127) / 128, nwg2 = tq * tp2;
         const char* force = getenv("PLORA_GEMM_TILE_P");
         const int fw = force ? atoi(force) : 0;
