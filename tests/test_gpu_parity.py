@@ -104,13 +104,15 @@ def test_shrink_tile_rows_bitwise_equal(P, monkeypatch):
 
 
 # (384, 704): pipelined forward with a feature tail at either width (704 % 256,
-# 704 % 128); (712, 640): the same for the backward GEMM (d_in = 712).
+# 704 % 128); (712, 640): the same for the backward GEMM (d_in = 712).  817
+# tokens: 4 token tiles (one group of 4); 1417: 6 (a group of 4 and one of 2).
+@pytest.mark.parametrize("first", [100, 700])
 @pytest.mark.parametrize("d_in,d_out", [(384, 704), (712, 640)])
-def test_tile_widths_bitwise_equal(P, d_in, d_out, monkeypatch):
+def test_tile_widths_bitwise_equal(P, d_in, d_out, first, monkeypatch):
     """Both tile widths and both L2 group sizes of the tile map give every
     output element the same MFMA sequence: equal bits."""
     import torch
-    wl = workloads.custom(d_in, d_out, [100, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
+    wl = workloads.custom(d_in, d_out, [first, 0, 513, 1, 163, 40], [16, 8, 64, 32, 1, 128],
                           [32.0, 16.0, 8.0, 16.0, 4.0, 256.0], "bf16", seed=31, name="tile_widths")
     log("case %s" % wl.name)
     inp = workloads.make_inputs(wl)
