@@ -886,6 +886,54 @@ def write_stats_profile(d, title, name):
     print(txt)
 
 
+BLOCK_COUNTER_CLASSES = (("attn_fwd_kernel", "attn_fwd"), ("attn_bwd_dq_kernel", "attn_bwd_dq"),
+                         ("attn_bwd_dkv_kernel", "attn_bwd_dkv"), ("gemm_lora_bf16_pipe<true", "gemm_fwd"),
+                         ("gemm_lora_bf16_pipe<false, 4, true>", "gemm_bwd_swiglu"),
+                         ("gemm_lora_bf16_pipe<false, 2, true>", "gemm_bwd_swiglu"),
+                         ("gemm_lora_bf16_pipe<false", "gemm_bwd"), ("shrink_bf16_pipe", "shrink"),
+                         ("wgrad_bf16_pipe", "wgrad"), ("wgrad_prep", "wgrad_prep"), ("rmsnorm", "rmsnorm"),
+                         ("swiglu", "swiglu"), ("rope_kernel", "rope"), ("add_kernel", "add"), ("adamw", "adamw"))
+
+
+def write_block_counters(d):
+    """Per-kernel-class counter summary of the decoder block from two rocprofv3
+    --pmc runs (p1/, p2/ under d; their commands in d/commands.json) into
+    profiles/kernels_llama3_8b_block_counters.txt."""
+    import csv
+    import glob
+    cmds = json.load(open(os.path.join(d, "commands.json")))
+    sums = {}
+    for run in ("p1", "p2"):
+        f = glob.glob(os.path.join(d, run, "**", "*counter_collection.csv"), recursive=True)[0]
+        for r in csv.DictReader(open(f)):
+            cls = next((c for key, c in BLOCK_COUNTER_CLASSES if key in r["Kernel_Name"]), None)
+            if cls is None:
+                continue
+            sums.setdefault(cls, {}).setdefault(r["Counter_Name"], 0.0)
+            sums[cls][r["Counter_Name"]] += float(r["Counter_Value"])
+    ratio = lambda a, b: a / b if b else float("nan")
+    lines = ["# matrix-core, vector-ALU and LDS counters per kernel class, Llama-3-8B decoder block "
+             "(32 adapters x 1024 tokens)",
+             "# pass 1: " + cmds["p1"], "# pass 2: " + cmds["p2"],
+             "# mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES); valu_active = "
+             "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES;",
+             "# lds_wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES; conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "
+             "valu/mfma = SQ_INSTS_VALU / SQ_INSTS_MFMA (instructions, summed over the run's dispatches)", "",
+             "%-16s %10s %11s %9s %10s %9s" % ("class", "mfma_util", "valu_active", "lds_wait", "conflict", "valu/mfma")]
+    order = [c for _, c in BLOCK_COUNTER_CLASSES]
+    for cls in sorted(sums, key=lambda c: order.index(c)):
+        v = sums[cls]
+        lines.append("%-16s %10.3f %11.3f %9.3f %10.4f %9.2f" % (
+            cls, ratio(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0), 4 * v.get("SQ_BUSY_CU_CYCLES", 0)),
+            ratio(v.get("SQ_ACTIVE_INST_VALU", 0), v.get("SQ_WAVE_CYCLES", 0)),
+            ratio(v.get("SQ_WAIT_INST_LDS", 0), v.get("SQ_WAVE_CYCLES", 0)),
+            ratio(v.get("SQ_LDS_BANK_CONFLICT", 0), v.get("SQ_LDS_IDX_ACTIVE", 0)),
+            ratio(v.get("SQ_INSTS_VALU", 0), v.get("SQ_INSTS_MFMA", 0))))
+    txt = "\n".join(lines) + "\n"
+    open(os.path.join(ROOT, "profiles", "kernels_llama3_8b_block_counters.txt"), "w").write(txt)
+    print(txt)
+
+
 def write_profiles(d, workload):
     import workloads
     wl = workloads.config(workload)
@@ -946,7 +994,9 @@ def main():
                          "write summaries under profiles/ and exit")
     args = ap.parse_args()
     if args.rocprof_summary:
-        if args.block:
+        if args.block and os.path.isdir(os.path.join(args.rocprof_summary, "p1")):
+            write_block_counters(args.rocprof_summary)
+        elif args.block:
             write_stats_profile(args.rocprof_summary, "Llama-3-8B decoder block, 32 adapters x 1024 tokens",
                                 "kernels_llama3_8b_block_stats.txt")
         elif args.decode:
