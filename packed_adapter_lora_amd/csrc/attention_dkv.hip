@@ -102,9 +102,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkv_kernel(AttnArgs a, SeqTab
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)(dbuf + r * kDkvRow), 16, vo, 0, 0, 0);
         }
         if (wu < 4) {
-            // piece wu: lse (wu < 2) or delta rows of heads 2*(wu%2) .. +1, 32 queries each
-            const int hh = 2 * (wu & 1) + (l >> 5);
-            const int64_t e = (int64_t)(hq0 + hh) * a.T + t0 + qt * kDkvQRows + (l & 31);
+            // piece wu: lse (wu < 2) or delta rows of heads 2*(wu%2) .. +1, 32 queries each.
+            // The lane terms come from an opaque copy of the lane id: a head
+            // offset held across the loop was spilled, and its reload's wait
+            // also waited for the stage in flight.
+            int lo = lane_id();
+            asm volatile("" : "+v"(lo));
+            const int hh = 2 * (wu & 1) + (lo >> 5);
+            const int64_t e = (int64_t)(hq0 + hh) * a.T + t0 + qt * kDkvQRows + (lo & 31);
             const uint32_t vo = (uint32_t)(e * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wu < 2 ? rl : rt,
                                                      (lds_void*)(lbuf + (wu >> 1) * 128 + 64 * (wu & 1)), 4, vo,
