@@ -280,18 +280,40 @@ int plora_backward_dAdB_acc(const plora_desc* d, const void* X, const void* dY, 
         __bf16* h_hi = wsb ? reinterpret_cast<__bf16*>(wsb + wl.ft_h) : nullptr;
         const WgradArgs wb{dY, H, dB, part_b, d->d_out, acc};
         const WgradArgs wa{X, G, dA, part_a, d->d_in, acc};
-        if (dB) {
-            e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st); });
+        // one launch for the transposes of H and G, the two weight-gradient
+        // passes, one launch for both passes' chunk reductions
+        const bool pipe_b = dB && wgrad_pipe_ok(wb, s, pb, h_hi);
+        const bool pipe_a = dA && wgrad_pipe_ok(wa, s, pa, g_hi);
+        const float* pf[2];
+        __bf16 *phi[2], *plo[2];
+        int np = 0;
+        if (pipe_b) pf[np] = H, phi[np] = h_hi, plo[np++] = h_hi + pb.ft_elems;
+        if (pipe_a) pf[np] = G, phi[np] = g_hi, plo[np++] = g_hi + pa.ft_elems;
+        if (np > 0) {
+            e = timed("wgrad", st, [&] { return launch_wgrad_prep(np, pf, phi, plo, s, pa, st); });
             if (e != hipSuccess) return hip_fail(e, "wgrad launch");
-            e = timed("reduce", st, [&] { return launch_wgrad_reduce(wb, s, pb, st); });
-            if (e != hipSuccess) return hip_fail(e, "reduce launch");
+        }
+        const WgradArgs* ra[2];
+        const WgradPlan* rp[2];
+        int nr = 0;
+        if (dB) {
+            e = timed("wgrad", st, [&] {
+                return pipe_b ? launch_wgrad_bf16_pipe(wb, s, pb, h_hi, h_hi + pb.ft_elems, st)
+                              : launch_wgrad_bf16(wb, s, pb, st);
+            });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+            ra[nr] = &wb, rp[nr++] = &pb;
         }
         if (dA) {
-            e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st); });
+            e = timed("wgrad", st, [&] {
+                return pipe_a ? launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st)
+                              : launch_wgrad_bf16(wa, s, pa, st);
+            });
             if (e != hipSuccess) return hip_fail(e, "wgrad launch");
-            e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
-            if (e != hipSuccess) return hip_fail(e, "reduce launch");
+            ra[nr] = &wa, rp[nr++] = &pa;
         }
+        e = timed("reduce", st, [&] { return launch_wgrad_reduce(nr, ra, rp, s, st); });
+        if (e != hipSuccess) return hip_fail(e, "reduce launch");
         return PLORA_OK;
     } catch (...) {
         return fail(PLORA_ERR_HIP, "unexpected exception");
@@ -419,9 +441,28 @@ int plora_backward_dA_shared(const plora_desc* d, const void* X, int np, const f
         wa.part_stride = (int64_t)(wl.part_stride / 4);
         wa.ft_stride = (int64_t)(wl.ft_stride / 2);
         wa.np = np;
-        e = timed("wgrad", st, [&] { return launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi ? g_hi + pa.ft_elems : nullptr, st); });
+        const bool pipe = wgrad_pipe_ok(wa, s, pa, g_hi);
+        if (pipe) {
+            // the np transposes in one launch (panel p's at p * ft_stride)
+            __bf16 *phi[3], *plo[3];
+            for (int p = 0; p < np; ++p) phi[p] = g_hi + p * wa.ft_stride, plo[p] = phi[p] + pa.ft_elems;
+            e = timed("wgrad", st, [&] { return launch_wgrad_prep(np, g, phi, plo, s, pa, st); });
+            if (e != hipSuccess) return hip_fail(e, "wgrad launch");
+        }
+        e = timed("wgrad", st, [&] {
+            return pipe ? launch_wgrad_bf16_pipe(wa, s, pa, g_hi, g_hi + pa.ft_elems, st) : launch_wgrad_bf16(wa, s, pa, st);
+        });
         if (e != hipSuccess) return hip_fail(e, "wgrad launch");
-        e = timed("reduce", st, [&] { return launch_wgrad_reduce(wa, s, pa, st); });
+        // the panels' chunk reductions in one launch
+        WgradArgs side[3];
+        const WgradArgs* ra[3];
+        const WgradPlan* rp[3];
+        for (int p = 0; p < np; ++p) {
+            side[p] = WgradArgs{X, g[p], dA[p], part ? part + p * wa.part_stride : nullptr, d->d_in, acc};
+            ra[p] = &side[p];
+            rp[p] = &pa;
+        }
+        e = timed("reduce", st, [&] { return launch_wgrad_reduce(np, ra, rp, s, st); });
         if (e != hipSuccess) return hip_fail(e, "reduce launch");
         return PLORA_OK;
     } catch (...) {

@@ -82,11 +82,22 @@ bool gemm_bf16_pipelined(const GemmArgs& a, const SegTable& s);
 hipError_t launch_shrink_bf16(const ShrinkArgs& a, const SegTable& s, const WorkMap& m, int32_t units,
                               hipStream_t st);
 hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);
-// Pipelined weight gradient: first writes the transposed hi/lo bf16 copy of F
-// (plan.ft_elems elements each) into fhi / flo, then reduces over tokens.
-hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, __bf16* fhi, __bf16* flo,
-                                  hipStream_t st);
-hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st);
+// Whether the pipelined weight-gradient kernel takes this reduction (ranks up
+// to 64, the transposed copy of F given, offsets within 32 bits).
+bool wgrad_pipe_ok(const WgradArgs& a, const SegTable& s, const WgradPlan& p, const __bf16* fhi);
+// The transposed hi/lo bf16 copies of nside (1..3) F's over the same segments
+// in one launch: F[k] into hi[k] / lo[k] (p.ft_elems elements each; the layout
+// does not depend on the feature width, so any plan of the call will do).
+hipError_t launch_wgrad_prep(int nside, const float* const* F, __bf16* const* hi, __bf16* const* lo,
+                             const SegTable& s, const WgradPlan& p, hipStream_t st);
+// Pipelined weight gradient over the copies launch_wgrad_prep wrote.
+hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, const __bf16* fhi,
+                                  const __bf16* flo, hipStream_t st);
+// The chunk reductions (and the zero rows of adapters without tokens) of
+// nside (1..3) weight-gradient passes of one call in one launch: pass k is a[k]
+// (single panel: a[k]->np <= 1) with plan p[k].
+hipError_t launch_wgrad_reduce(int nside, const WgradArgs* const* a, const WgradPlan* const* p, const SegTable& s,
+                               hipStream_t st);
 
 // Per-adapter AdamW over one packed panel [R][D] (fp32 master P, moments m, v,
 // gradient g; optional operator copy `out` of dtype out_dtype).  The factors

@@ -457,9 +457,10 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 // wgrad_prep writes the fp32 H_i (or G_i) block [n_i][r_i] transposed as two
 // bf16 arrays hi = bf16(v), lo = bf16(v - hi), row j of length pad64(n_i)
 // (zero-padded), so the main kernel can stream it as whole 128-byte lines.
-// One workgroup per (64-token block, adapter): the block's 64 rows of r_i
-// values are contiguous in H, so they are read whole, transposed in LDS, and
-// leave as r_i pieces of 128 bytes per array.
+// One workgroup per (64-token block, adapter, side): the block's 64 rows of
+// r_i values are contiguous in H, so they are read whole, transposed in LDS,
+// and leave as r_i pieces of 128 bytes per array.  The sides (H and G of one
+// call, or the G's of a shared-input pass) share one launch.
 //
 // wgrad_bf16_pipe: one workgroup per (adapter token chunk, 256 features), the
 // feature tiles fastest so the workgroups running together read whole rows.
@@ -470,7 +471,17 @@ __global__ __launch_bounds__(256) void wgrad_bf16(WgradArgs a, SegTable seg, Wgr
 // register-staged kernel above).  Tokens past the chunk read as zero
 // (outside the buffer range or zero padding).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void wgrad_prep(const float* F, bf16* hi, bf16* lo, SegTable seg, WgradPlan plan) {
+struct PrepSides {
+    const float* F[3];
+    bf16* hi[3];
+    bf16* lo[3];
+};
+
+__global__ __launch_bounds__(256) void wgrad_prep(PrepSides ps, SegTable seg, WgradPlan plan) {
+    const int z = (int)blockIdx.z;
+    const float* const F = z == 0 ? ps.F[0] : z == 1 ? ps.F[1] : ps.F[2];
+    bf16* const hi = z == 0 ? ps.hi[0] : z == 1 ? ps.hi[1] : ps.hi[2];
+    bf16* const lo = z == 0 ? ps.lo[0] : z == 1 ? ps.lo[1] : ps.lo[2];
     const int i = (int)blockIdx.y;
     const int64_t n = seg.off[i + 1] - seg.off[i];
     const int64_t u0 = (int64_t)blockIdx.x * 64;
@@ -717,19 +728,39 @@ __global__ __launch_bounds__(256, 1) void wgrad_bf16_pipe(WgradArgs a, SegTable 
 // out rows of adapters whose tokens span 0 or >= 2 chunks:
 // out = s_i * sum_u partial[u] in chunk order (0 for an empty adapter), or
 // out += that when accumulating (an empty adapter is then left alone).
-__global__ __launch_bounds__(256) void wgrad_reduce(WgradArgs a, SegTable seg, WgradPlan plan) {
+// Side z (blockIdx.z) is one weight-gradient pass of the call (dB, dA, or a
+// panel of a shared-input pass); only the per-adapter fields the reduction
+// reads travel as kernel arguments.
+struct ReduceSide {
+    float* out;
+    const float* part;
+    int64_t D;
+    int64_t part_off[kMaxN + 1];
+    int32_t pre[kMaxN + 1];
+};
+struct ReduceArgs {
+    ReduceSide side[3];
+    int32_t rank[kMaxN];
+    int32_t roff[kMaxN];
+    float scale[kMaxN];
+    int32_t accumulate;
+};
+static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments");
+
+__global__ __launch_bounds__(256) void wgrad_reduce(ReduceArgs ra) {
     const int i = (int)blockIdx.y;
-    const int nch = plan.chunks.pre[i + 1] - plan.chunks.pre[i];
-    if (nch == 1 || (nch == 0 && a.accumulate)) return;
-    const int64_t n = (int64_t)seg.rank[i] * a.D;  // multiple of 8
-    const float sc = seg.scale[i];
-    float* __restrict__ out = a.out + (int64_t)seg.roff[i] * a.D;
-    const float* __restrict__ part = a.part + plan.part_off[i];
+    const ReduceSide& sd = ra.side[blockIdx.z];
+    const int nch = sd.pre[i + 1] - sd.pre[i];
+    if (nch == 1 || (nch == 0 && ra.accumulate)) return;
+    const int64_t n = (int64_t)ra.rank[i] * sd.D;  // multiple of 8
+    const float sc = ra.scale[i];
+    float* __restrict__ out = sd.out + (int64_t)ra.roff[i] * sd.D;
+    const float* __restrict__ part = sd.part + sd.part_off[i];
     for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (int64_t)gridDim.x * 1024) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
         for (int u = 0; u < nch; ++u) s += *reinterpret_cast<const f32x4*>(part + (int64_t)u * n + e);
         f32x4 o = s * sc;
-        if (a.accumulate) o += *reinterpret_cast<const f32x4*>(out + e);
+        if (ra.accumulate) o += *reinterpret_cast<const f32x4*>(out + e);
         *reinterpret_cast<f32x4*>(out + e) = o;
     }
 }
@@ -894,28 +925,33 @@ hipError_t launch_wgrad_bf16(const WgradArgs& a, const SegTable& s, const WgradP
             hipLaunchKernelGGL((wgrad_bf16_pipe<MAXJT, NCT, 1>), grid, block, 0, st, a, s, p, fhi, flo);  \
     } while (0)
 
-hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, bf16* fhi, bf16* flo,
-                                  hipStream_t st) {
-    const int64_t tk = p.chunk_tokens;
-    const int np = a.np > 1 ? a.np : 1;
+bool wgrad_pipe_ok(const WgradArgs& a, const SegTable& s, const WgradPlan& p, const bf16* fhi) {
     // (the pipelined grid puts the chunks in y: at most 65535 of them)
-    if (s.rmax > 64 || fhi == nullptr || tk * a.D * 2 >= (int64_t(1) << 31) || p.chunks.pre[s.n] > 65535)
-        return launch_wgrad_bf16(a, s, p, st);
-    const int R = s.roff[s.n];
-    if (R > 0) {
-        int64_t maxnp = 0;
-        for (int i = 0; i < s.n; ++i) maxnp = maxnp > pad64(s.off[i + 1] - s.off[i]) ? maxnp : pad64(s.off[i + 1] - s.off[i]);
-        if (maxnp > 0) {
-            // (hi/lo offsets are multiples of 64 elements and the arrays start 16-byte aligned)
-            for (int q = 0; q < np; ++q) {
-                const float* F = q == 0 ? a.F : q == 1 ? a.F1 : a.F2;
-                hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)(maxnp / 64), (unsigned)s.n), dim3(256), 0, st, F,
-                                   fhi + q * a.ft_stride, flo + q * a.ft_stride, s, p);
-                const hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-            }
-        }
+    return s.rmax <= 64 && fhi != nullptr && (int64_t)p.chunk_tokens * a.D * 2 < (int64_t(1) << 31) &&
+           p.chunks.pre[s.n] <= 65535;
+}
+
+hipError_t launch_wgrad_prep(int nside, const float* const* F, bf16* const* hi, bf16* const* lo, const SegTable& s,
+                             const WgradPlan& p, hipStream_t st) {
+    if (nside < 1 || nside > 3) return hipErrorInvalidValue;
+    int64_t maxnp = 0;
+    for (int i = 0; i < s.n; ++i) maxnp = maxnp > pad64(s.off[i + 1] - s.off[i]) ? maxnp : pad64(s.off[i + 1] - s.off[i]);
+    if (maxnp == 0 || s.roff[s.n] == 0) return hipSuccess;
+    PrepSides ps{};
+    for (int k = 0; k < nside; ++k) {
+        ps.F[k] = F[k];
+        ps.hi[k] = hi[k];
+        ps.lo[k] = lo[k];
     }
+    // (hi/lo offsets are multiples of 64 elements and the arrays start 16-byte aligned)
+    hipLaunchKernelGGL(wgrad_prep, dim3((unsigned)(maxnp / 64), (unsigned)s.n, (unsigned)nside), dim3(256), 0, st, ps,
+                       s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const WgradPlan& p, const bf16* fhi,
+                                  const bf16* flo, hipStream_t st) {
+    const int np = a.np > 1 ? a.np : 1;
     const int32_t units = p.chunks.pre[s.n];
     if (units <= 0) return hipSuccess;
     // 128-feature workgroups when the 256-feature grid would not give every CU
@@ -937,21 +973,37 @@ hipError_t launch_wgrad_bf16_pipe(const WgradArgs& a, const SegTable& s, const W
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad_reduce(const WgradArgs& a, const SegTable& s, const WgradPlan& p, hipStream_t st) {
-    bool any = false;
-    for (int i = 0; i < s.n; ++i) any |= (p.chunks.pre[i + 1] - p.chunks.pre[i]) != 1;
-    if (!any || s.n == 0) return hipSuccess;
-    const int64_t n = (int64_t)s.rmax * a.D;
+hipError_t launch_wgrad_reduce(int nside, const WgradArgs* const* a, const WgradPlan* const* p, const SegTable& s,
+                               hipStream_t st) {
+    if (nside < 0 || nside > 3) return hipErrorInvalidValue;
+    ReduceArgs ra{};
+    int z = 0;
+    int64_t dmax = 0;
+    for (int k = 0; k < nside; ++k) {
+        bool any = false;  // a side with nothing to reduce or zero is left out
+        for (int i = 0; i < s.n; ++i) any |= (p[k]->chunks.pre[i + 1] - p[k]->chunks.pre[i]) != 1;
+        if (!any) continue;
+        ReduceSide& sd = ra.side[z++];
+        sd.out = a[k]->out;
+        sd.part = a[k]->part;
+        sd.D = a[k]->D;
+        for (int i = 0; i <= s.n; ++i) {
+            sd.part_off[i] = p[k]->part_off[i];
+            sd.pre[i] = p[k]->chunks.pre[i];
+        }
+        dmax = dmax > sd.D ? dmax : sd.D;
+        ra.accumulate = a[k]->accumulate;
+    }
+    if (z == 0 || s.n == 0) return hipSuccess;
+    for (int i = 0; i < s.n; ++i) {
+        ra.rank[i] = s.rank[i];
+        ra.roff[i] = s.roff[i];
+        ra.scale[i] = s.scale[i];
+    }
+    const int64_t n = (int64_t)s.rmax * dmax;
     int64_t bx = (n / 4 + 255) / 256;
     if (bx > 1024) bx = 1024;
-    const dim3 grid((unsigned)bx, (unsigned)s.n), block(256);
-    const int np = a.np > 1 ? a.np : 1;
-    for (int q = 0; q < np; ++q) {
-        if (np == 1)
-            hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, a, s, p);
-        else
-            hipLaunchKernelGGL(wgrad_reduce, grid, block, 0, st, wgrad_single(a, q), s, p);
-    }
+    hipLaunchKernelGGL(wgrad_reduce, dim3((unsigned)bx, (unsigned)s.n, (unsigned)z), dim3(256), 0, st, ra);
     return hipGetLastError();
 }
 
