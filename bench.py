@@ -381,13 +381,27 @@ def measure_ceilings():
     wg = cus  # one wave per SIMD
     t32 = sustained(0, ops)
     t16 = sustained(1, ops)
+    t32l = sustained(2, ops)
     zeros = torch.zeros_like(ops)
     z32 = sustained(0, zeros)
     res = {"mfma_bf16_tflops": round(max(t32, t16), 1), "mfma_32x32x16_tflops": round(t32, 1),
-           "mfma_16x16x32_tflops": round(t16, 1), "mfma_32x32x16_zero_operands_tflops": round(z32, 1),
+           "mfma_16x16x32_tflops": round(t16, 1), "mfma_32x32x16_lds_fed_tflops": round(t32l, 1),
+           "mfma_32x32x16_zero_operands_tflops": round(z32, 1),
            "mfma_probe": "%d workgroups x 4 waves (one per SIMD), each a 128x128 block of accumulators in registers "
-                         "fed random bf16 operands, back-to-back launches for 1.5 s, the last 0.75 s timed" % wg}
+                         "fed random bf16 operands (lds_fed: the operands read back from LDS at every step, 512 B "
+                         "per instruction as in the GEMM), back-to-back launches for 1.5 s, the last 0.75 s timed"
+                         % wg}
     del zeros, ops
+    # L2 -> LDS: every wave streams a 2 MiB buffer (L2-resident) into LDS
+    span, dwg, dit = 2 << 20, 2 * cus, 100
+    dsrc = torch.ones((span // 4,), dtype=torch.float32, device="cuda")
+    dout = torch.empty((dwg * 256,), dtype=torch.int32, device="cuda")
+    nb_dma = [0.0]
+    ms = timed(lambda: nb_dma.__setitem__(0, P.plora_probe_lds_dma(dsrc, dwg, dit, dout)))
+    res["lds_dma_l2_GBps"] = round(nb_dma[0] / (ms * 1e-3) / 1e9, 1)
+    res["lds_dma_probe"] = ("%d workgroups x 4 waves, each streaming a 2 MiB buffer %d times into LDS with 16-byte "
+                            "buffer loads that write LDS, 6 in flight per wave" % (dwg, dit))
+    del dsrc, dout
     nbytes = 2 << 30
     src = torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)

@@ -122,6 +122,8 @@ def _load():
                                             ctypes.POINTER(ctypes.c_double), vp]),
         "plora_probe_copy": (ctypes.c_int, [vp, vp, ctypes.c_size_t, ctypes.c_int32, vp]),
         "plora_probe_read": (ctypes.c_int, [vp, ctypes.c_size_t, ctypes.c_int32, vp, vp]),
+        "plora_probe_lds_dma": (ctypes.c_int, [vp, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, vp,
+                                               ctypes.POINTER(ctypes.c_double), vp]),
         "plora_h_elems": (ctypes.c_size_t, [dp]),
         "plora_workspace_bytes": (ctypes.c_size_t, [dp]),
         "plora_validate": (ctypes.c_int, [dp]),
@@ -405,8 +407,9 @@ def plora_probe_mfma_operand_bytes() -> int:
 
 
 def plora_probe_mfma(operands, workgroups, iters, out, shape=0, stream=None) -> float:
-    """Enqueues the sustained-MFMA probe (shape 0: 32x32x16, 1: 16x16x32);
-    returns the launch's FLOP count."""
+    """Enqueues the sustained-MFMA probe (shape 0: 32x32x16, 1: 16x16x32,
+    2: 32x32x16 with the operands read from LDS); returns the launch's FLOP
+    count."""
     if operands.numel() * operands.element_size() < plora_probe_mfma_operand_bytes():
         raise ValueError("operand buffer smaller than plora_probe_mfma_operand_bytes()")
     if out.numel() < workgroups * 256 or str(out.dtype) != "torch.float32":
@@ -435,6 +438,19 @@ def plora_probe_read(src, out, workgroups=2048, stream=None):
         _check_tensor(n, t, tuple(t.shape), None)
     _check(_lib.plora_probe_read(_addr(src), src.numel() * src.element_size(), int(workgroups), _addr(out),
                                  _stream(stream)))
+
+
+def plora_probe_lds_dma(src, workgroups, iters, out, stream=None) -> float:
+    """Enqueues the L2 -> LDS probe over all of src (a multiple of 4096
+    bytes); returns the bytes the launch moves."""
+    if out.numel() < workgroups * 256 or out.element_size() != 4:
+        raise ValueError("out needs workgroups * 256 32-bit values")
+    for n, t in (("src", src), ("out", out)):
+        _check_tensor(n, t, tuple(t.shape), None)
+    nb = ctypes.c_double(0.0)
+    _check(_lib.plora_probe_lds_dma(_addr(src), src.numel() * src.element_size(), int(workgroups), int(iters),
+                                    _addr(out), ctypes.byref(nb), _stream(stream)))
+    return float(nb.value)
 
 
 def plora_h_elems(desc: Desc) -> int:

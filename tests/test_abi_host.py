@@ -347,3 +347,21 @@ def test_dx_swiglu_error_paths(P):
     assert lib.plora_backward_dx_swiglu(desc(P, ranks=(4, 0, 16)).ref(), *args, None) == -3
     n0 = P.Desc([0, 0], [8], [16.0], 64, 32, "bf16")
     assert lib.plora_backward_dx_swiglu(n0.ref(), *([None] * 9), None) == 0
+
+
+def test_probe_error_paths(P):
+    """The ceiling probes reject bad arguments on the host, before any launch."""
+    lib = P._lib
+    fl = ctypes.c_double(0.0)
+    assert lib.plora_probe_mfma(0x1000, 3, 1, 1, 0x2000, ctypes.byref(fl), None) == -5  # shape 0..2
+    assert lib.plora_probe_mfma(None, 0, 1, 1, 0x2000, ctypes.byref(fl), None) == -1
+    assert lib.plora_probe_mfma(0x1000, 2, 0, 1, 0x2000, ctypes.byref(fl), None) == -5
+    assert lib.plora_probe_mfma(0x1008, 2, 1, 1, 0x2000, ctypes.byref(fl), None) == -9
+    nb = ctypes.c_double(0.0)
+    assert lib.plora_probe_lds_dma(0x1000, 4096 + 16, 1, 1, 0x2000, ctypes.byref(nb), None) == -5
+    assert lib.plora_probe_lds_dma(0x1000, 0, 1, 1, 0x2000, ctypes.byref(nb), None) == -5
+    assert lib.plora_probe_lds_dma(0x1000, (1 << 30) + 4096, 1, 1, 0x2000, ctypes.byref(nb), None) == -5
+    assert lib.plora_probe_lds_dma(0x1000, 4096, 0, 1, 0x2000, ctypes.byref(nb), None) == -5
+    assert lib.plora_probe_lds_dma(None, 4096, 1, 1, 0x2000, ctypes.byref(nb), None) == -1
+    assert lib.plora_probe_lds_dma(0x1000, 4096, 1, 1, 0x2004, ctypes.byref(nb), None) == -9
+    assert "aligned" in P.plora_last_error()
